@@ -1,0 +1,274 @@
+"""Pins of the oracle's full step: the window ring, AdamStats against Adam's
+textbook recurrence in double, the closed forms at m = 1 and t = 1, update
+sparsity (last paragraph of the MicroAdam page) and the memory arithmetic of
+its second paragraph."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _grads(rng, d, scale=1e-3, outlier=0.01):
+    g = (rng.standard_normal(d) * scale).astype(np.float32)
+    g[rng.random(d) < outlier] *= 50
+    return O.bf16_rne(g)
+
+
+def _entries(row):
+    return (row & 0xffff).astype(np.int64), O.bf16_to_f32((row >> 16).astype(np.uint16))
+
+
+def _row_as_dense(cfg, G, i):
+    """Scatter window row i of the full G into a dense length-d vector."""
+    d = cfg.d
+    out = np.zeros(d, np.float64)
+    for j in range(O.num_blocks(cfg)):
+        s, n = O.block_range(cfg, j)
+        off, kb = O.block_quota(cfg, j)
+        I, V = _entries(G[i * cfg.k + off: i * cfg.k + off + kb])
+        out[s + I] = V
+    return out
+
+
+def test_first_step_accumulator_is_the_gradient():
+    # zero initial state: a_1 = g_1 exactly, so the stored values are bf16(g) = g
+    rng = np.random.default_rng(20)
+    d, B = 50_000, 4096
+    cfg = O.make_cfg(d, B, d // 100, 4)
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    g = _grads(rng, d)
+    st.step(theta, g)
+    gf = O.bf16_to_f32(g)
+    for j in range(O.num_blocks(cfg)):
+        s, n = O.block_range(cfg, j)
+        off, kb = O.block_quota(cfg, j)
+        I, V = _entries(st.G[1 * cfg.k + off: 1 * cfg.k + off + kb])
+        np.testing.assert_array_equal(I, np.sort(O.topk(gf[s:s + n], kb)))
+        np.testing.assert_array_equal(V, gf[s + I])
+
+
+def test_ring_rotation():
+    rng = np.random.default_rng(21)
+    d, B, m = 20_000, 1000, 3
+    cfg = O.make_cfg(d, B, d // 50, m)
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    history = []
+    for t in range(1, 8):
+        before = st.G.copy().reshape(m, -1)
+        st.step(theta, _grads(rng, d))
+        after = st.G.reshape(m, -1)
+        row = t % m
+        for i in range(m):
+            if i != row:
+                np.testing.assert_array_equal(after[i], before[i])
+        history.append(after[row].copy())
+        # the rows hold exactly the last min(t, m) selections
+        held = {tuple(after[i]) for i in range(m) if t >= m or i in [(t - q) % m for q in range(t)]}
+        assert held == {tuple(h) for h in history[-min(t, m):]}
+
+
+def test_adamstats_m1_closed_form_no_ef():
+    # m = 1 and no error feedback: m_hat = c1*V and v_hat = c2*V^2 on I_t, 0 elsewhere
+    rng = np.random.default_rng(22)
+    d, B = 30_000, 2048
+    cfg = O.make_cfg(d, B, d // 100, 1, flags=O.FLAG_NO_EF)
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    for t in range(1, 6):
+        g = _grads(rng, d)
+        mh, vh = st.step(theta, g, moments=True)
+        _, _, c1, c2, _ = O.step_constants(cfg, t)
+        V = _row_as_dense(cfg, st.G, 0).astype(np.float32)
+        np.testing.assert_array_equal(mh, c1 * V)
+        np.testing.assert_array_equal(vh, c2 * (V * V))
+        # no error feedback: the selection is T_k of g itself
+        gf = O.bf16_to_f32(g)
+        nz = np.flatnonzero(V)
+        assert np.all(V[nz] == gf[nz])
+
+
+@pytest.mark.parametrize("ef", [True, False])
+def test_adamstats_matches_adam_recurrence(ef):
+    """t <= m: m_hat equals Adam's bias-corrected first moment of the sparse
+    gradient sequence s_tau = scatter(I_tau, V_tau); t > m: the window keeps the
+    last m terms, i.e. (m_t - beta^m m_{t-m}) / (1 - beta^t).  Same for v_hat
+    with beta2 and s^2.  Reference in double from the recurrence."""
+    rng = np.random.default_rng(23 + ef)
+    d, B, m = 40_000, 4096, 4
+    cfg = O.make_cfg(d, B, d // 100, m, flags=0 if ef else O.FLAG_NO_EF)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    M1 = [np.zeros(d)]
+    M2 = [np.zeros(d)]
+    for t in range(1, 11):
+        mh, vh = st.step(theta, _grads(rng, d), moments=True)
+        s = _row_as_dense(cfg, st.G, t % m)
+        M1.append(b1 * M1[-1] + (1 - b1) * s)
+        M2.append(b2 * M2[-1] + (1 - b2) * s * s)
+        if t <= m:
+            ref1, ref2 = M1[t] / (1 - b1 ** t), M2[t] / (1 - b2 ** t)
+        else:
+            ref1 = (M1[t] - b1 ** m * M1[t - m]) / (1 - b1 ** t)
+            ref2 = (M2[t] - b2 ** m * M2[t - m]) / (1 - b2 ** t)
+        # fp32 accumulation of at most m terms: error below (m + 4) ulps of the
+        # sum of magnitudes
+        mag1 = np.zeros(d)
+        mag2 = np.zeros(d)
+        for r in range(min(t, m)):
+            sr = _row_as_dense(cfg, st.G, (t - r) % m)
+            mag1 += b1 ** r * np.abs(sr)
+            mag2 += b2 ** r * sr * sr
+        c1 = (1 - b1) / (1 - b1 ** t)
+        c2 = (1 - b2) / (1 - b2 ** t)
+        # plus the double reference's own cancellation error when t > m
+        dbl1 = 1e-14 * (np.abs(M1[t]) + np.abs(M1[max(t - m, 0)])) / (1 - b1 ** t)
+        dbl2 = 1e-14 * (np.abs(M2[t]) + np.abs(M2[max(t - m, 0)])) / (1 - b2 ** t)
+        tol1 = (m + 4) * 2.0 ** -24 * c1 * mag1 + dbl1 + 1e-37
+        tol2 = (m + 4) * 2.0 ** -24 * c2 * mag2 + dbl2 + 1e-37
+        assert np.all(np.abs(mh - ref1) <= tol1)
+        assert np.all(np.abs(vh - ref2) <= tol2)
+
+
+def test_first_update_is_signlike_and_sparse():
+    # t = 1: m_hat = V, v_hat = V^2, so theta moves by lr*V/(|V| + eps) on I_1
+    rng = np.random.default_rng(24)
+    d, B = 60_000, 16384
+    cfg = O.make_cfg(d, B, d // 100, 10, lr=1e-4)
+    st = O.FullState(cfg)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    theta = theta0.copy()
+    g = _grads(rng, d)
+    st.step(theta, g)
+    V = _row_as_dense(cfg, st.G, 1)
+    moved = theta.astype(np.float64) - theta0
+    sel = V != 0
+    expect = -1e-4 * V[sel] / (np.abs(V[sel]) + 1e-8)
+    np.testing.assert_allclose(moved[sel], expect, rtol=0, atol=2e-9)
+    assert np.all(np.sign(moved[sel]) == -np.sign(V[sel]))
+    # untouched parameters are bitwise unchanged
+    np.testing.assert_array_equal(theta[~sel].view(np.uint32), theta0[~sel].view(np.uint32))
+
+
+def test_update_sparsity_bound():
+    # at most m*k parameters change per step: sparsity >= 1 - mk/d (90% at m=10, k=d/100)
+    rng = np.random.default_rng(25)
+    d, B, m = 2**18, 16384, 10
+    cfg = O.make_cfg(d, B, d // 100, m)
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    for t in range(1, 16):
+        before = theta.copy()
+        st.step(theta, _grads(rng, d))
+        changed = np.count_nonzero(theta.view(np.uint32) != before.view(np.uint32))
+        union = np.zeros(d, bool)
+        for i in range(m):
+            union |= _row_as_dense(cfg, st.G, i) != 0
+        assert changed <= union.sum() <= m * cfg.k
+        assert 1 - changed / d >= 1 - m * cfg.k / d >= 0.9 - 1e-3
+
+
+def test_decoupled_weight_decay_is_dense():
+    rng = np.random.default_rng(26)
+    d, B = 10_000, 1000
+    cfg = O.make_cfg(d, B, d // 100, 5, lr=1e-2, wd=0.1)
+    st = O.FullState(cfg)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    theta = theta0.copy()
+    st.step(theta, _grads(rng, d))
+    V = _row_as_dense(cfg, st.G, 1)
+    untouched = V == 0
+    decay = np.float32(1 - 1e-3)
+    np.testing.assert_array_equal(theta[untouched], theta0[untouched] * decay)
+
+
+def test_block_state_equals_full_state():
+    # blocks are independent: a detached block evolves exactly like its slice
+    rng = np.random.default_rng(27)
+    d, B, m = 70_001, 4096, 3
+    cfg = O.make_cfg(d, B, d // 100, m)
+    full = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    nb = O.num_blocks(cfg)
+    blocks = {j: O.BlockState.zeros(cfg, j) for j in (0, 5, nb - 1)}
+    btheta = {j: theta[slice(*(lambda s, n: (s, s + n))(*O.block_range(cfg, j)))].copy() for j in blocks}
+    for t in range(1, 7):
+        g = _grads(rng, d)
+        full.step(theta, g)
+        for j, bs in blocks.items():
+            s, n = O.block_range(cfg, j)
+            bs.step(btheta[j], g[s:s + n])
+            np.testing.assert_array_equal(btheta[j], theta[s:s + n])
+            off, kb = O.block_quota(cfg, j)
+            for i in range(m):
+                np.testing.assert_array_equal(bs.gseg[i], full.G[i * cfg.k + off: i * cfg.k + off + kb])
+            np.testing.assert_array_equal(bs.codes(), O.unpack_nibbles(full.ef, n, s))
+            np.testing.assert_array_equal(bs.stats, full.stats[2 * j: 2 * j + 2])
+
+
+def test_odd_block_length_nibbles_straddle():
+    # B odd: blocks share EF bytes; per-element nibble order must still hold
+    rng = np.random.default_rng(28)
+    d, B = 1001, 77
+    cfg = O.make_cfg(d, B, 50, 2)
+    full = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    for _ in range(3):
+        full.step(theta, _grads(rng, d))
+    codes = O.unpack_nibbles(full.ef, d)
+    assert codes.max() <= 15
+    # every block's minimum residual maps to code 0 somewhere
+    for j in range(O.num_blocks(cfg)):
+        s, n = O.block_range(cfg, j)
+        assert codes[s:s + n].min() == 0
+
+
+def test_global_quantizer_lemma1():
+    # the literal scalar (delta, Delta) over all of d: Lemma 1 with n = d
+    rng = np.random.default_rng(29)
+    d, B = 100_000, 8192
+    cfg = O.make_cfg(d, B, d // 100, 2, flags=O.FLAG_GLOBAL_QUANT)
+    st = O.FullState(cfg)
+    assert st.stats.size == 2
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    g = _grads(rng, d)
+    st.step(theta, g)
+    # reconstruct the residual a_1 = g with the selected entries zeroed
+    a = O.bf16_to_f32(g).astype(np.float32).copy()
+    V = _row_as_dense(cfg, st.G, 1)
+    a[V != 0] = 0
+    lo, hi = st.stats
+    assert lo == a.min() and hi == a.max()
+    xh = O.dequant_group(O.unpack_nibbles(st.ef, d), lo, hi)
+    err = np.linalg.norm(xh.astype(np.float64) - a)
+    omega = np.sqrt(d - 2) / 15 * (hi - lo) / np.sqrt(float(hi) ** 2 + float(lo) ** 2)
+    assert err <= omega * np.linalg.norm(a.astype(np.float64))
+
+
+def test_state_bytes_and_memory_paragraph():
+    with open(os.path.join(GOLDEN, "microadam_memory_paragraph.json")) as f:
+        page = json.load(f)
+    d = page["llama2_7b_d"]
+    m = page["m"]
+    k = d // 100
+    cfg = O.make_cfg(d, 16384, k, m)
+    sb = O.state_bytes(cfg)
+    assert sb == (d + 1) // 2 + 4 * m * k
+    gib = 2 ** 30
+    assert round(sb / gib, 2) == page["microadam_state_GB"]
+    assert round(2 * d / gib, 2) == page["adamw_8bit_state_GB"]
+    assert round(8 * d / gib, 2) == page["adamw_fp32_state_GB"]
+    assert abs(sb / d - page["state_over_d_at_m10"]) < 1e-3
+    # break-even window: 0.5d + 4m d/100 < 2d  <=>  m < 37.5
+    assert 0.5 + 4 * page["m_max"] / 100 == 2.0
+    for mm, below in ((37, True), (38, False)):
+        c = O.make_cfg(13015449600, 16384, 13015449600 // 100, mm)
+        assert (O.state_bytes(c) < 2 * 13015449600) == below
+    assert 1 - m * k / d >= page["min_update_sparsity_at_m10"] - 1e-9
