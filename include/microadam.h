@@ -1,0 +1,158 @@
+/*
+ * libmicroadam -- the MicroAdam optimizer step on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one on the page "MicroAdam (Sparse-Gradient Adaptive
+ * Optimization with Quantized Error Feedback)".  Its first paragraph defines
+ * one step t over a flat parameter vector of length d:
+ *
+ *   a_t = g_t + Q^{-1}(e_t, delta_t, Delta_t)     accumulate the 4-bit error
+ *   (I_t, V_t) = T_k(|a_t|)                       block-wise Top-k, k = d/100,
+ *                                                 int16 indices relative to
+ *                                                 blocks of B_d < 2^15 - 1
+ *   a_t[I_t] = 0;  e_{t+1} = Q(a_t, ...)          requantize the residual, b = 4
+ *   G[t mod m] = (I_t, V_t)                       circular window of m rows
+ *   m_hat = AdamStats(beta1, G), v_hat = AdamStats(beta2, G^2)
+ *                                                 z[I_i] += beta^r V_i
+ * and the parameters take an AdamW step with (m_hat, v_hat).  Its second
+ * paragraph counts the state: 0.5d bytes of codes and 4mk bytes of window.
+ *
+ * Layouts (device memory, all owned by the library unless stated):
+ *   codes   u8[ceil(d/2)]  element i in byte i/2, low nibble for even i
+ *   stats   f32[2*n_b]     per block j: {delta_j, Delta_j} (min and max of the
+ *                          block's residual; one pair per block)
+ *   window  u32[m][k]      row r holds k entries; block j's k_b(j) entries start
+ *                          at offset floor(k*s_j/d) of every row, ascending in
+ *                          index; entry = index | bf16_bits(V) << 16
+ * with n_b = ceil(d/B_d), block j = [s_j, e_j) = [j*B_d, min((j+1)*B_d, d)) and
+ * k_b(j) = floor(k*e_j/d) - floor(k*s_j/d).
+ *
+ * Errors: functions return 0 or a negative MA_E* code (pointer-returning ones
+ * return NULL).  The code and a message are kept per calling thread
+ * (ma_last_error, ma_last_error_message).  Nothing here prints or aborts.
+ *
+ * Streams: ma_step and ma_debug_moments only enqueue work on the stream given
+ * and never synchronize.  The state/accessor calls marked "synchronous" wait
+ * for the whole device.  Calls on one handle must not overlap.
+ */
+#ifndef MICROADAM_H
+#define MICROADAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ma_ctx ma_ctx;
+
+enum {
+    MA_OK = 0,
+    MA_EINVAL = -1,         /* bad argument: null or misaligned pointer, out-of-range value */
+    MA_EUNSUPPORTED = -2,   /* valid for the method but not built here (b != 4) */
+    MA_ENOMEM = -3,         /* device allocation failed; nothing is leaked */
+    MA_EHIP = -4,           /* a HIP call or kernel launch failed */
+};
+
+/* Flags for ma_set_flags. */
+#define MA_FLAG_NO_EF 1u        /* a_t = g_t: stored error neither read nor rewritten */
+#define MA_FLAG_FORCE_DENSE 4u  /* stream all of theta in the update (same results) */
+
+/* State buffers for ma_read_state / ma_write_state. */
+#define MA_STATE_CODES 0
+#define MA_STATE_STATS 1
+#define MA_STATE_WINDOW 2
+
+/*
+ * Creates an optimizer for d parameters (first paragraph of the MicroAdam
+ * page: blocks of B_d < 2^15 - 1, Top-k budget k per step, window of m rows,
+ * b-bit error quantizer; AdamW hyperparameters beta1, beta2, eps, lr, wd;
+ * seed keys the quantizer's counter-based random numbers on (seed, step,
+ * element)).  Requires d >= 1, 1 <= B_d <= 32766, 0 <= k <= d, m >= 1,
+ * 0 <= beta < 1, eps > 0, finite lr and wd >= 0; b must be 4
+ * (MA_EUNSUPPORTED otherwise).  Allocates and zero-fills all state on the
+ * current HIP device (so e_1 = 0 and unwritten window rows add nothing);
+ * step count t = 0.  Returns NULL on error.
+ */
+ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float beta1,
+                  float beta2, float eps, float lr, float wd, uint64_t seed);
+
+/*
+ * One MicroAdam step (t -> t+1).  params: caller-owned device f32[d], updated
+ * in place.  grads: caller-owned device bf16[d] (raw bits), read only.  Both
+ * must be element-aligned and live on the handle's device.  Enqueued on
+ * `stream`, asynchronous.  Returns MA_OK, MA_EINVAL (null/misaligned pointer)
+ * or MA_EHIP (launch error); t advances only on success.
+ */
+int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream);
+
+/* Optimizer-state bytes the second paragraph of the MicroAdam page counts:
+ * ceil(d/2) + 4*m*k (0.9d at m = 10, k = d/100).  0 for NULL. */
+size_t ma_state_bytes(const ma_ctx *h);
+
+/* Everything else the library holds on the device: per-block statistics
+ * (8*n_b), the block offset table (8*(n_b+1)), the beta-power table (8*m) and
+ * the code buffer's tail padding.  0 for NULL. */
+size_t ma_aux_bytes(const ma_ctx *h);
+
+/* Frees every device buffer of the handle; NULL is accepted. */
+void ma_destroy(ma_ctx *h);
+
+/* Last error code / message of the calling thread (MA_OK / "" if none). */
+int ma_last_error(void);
+const char *ma_last_error_message(void);
+
+/* Accessors. */
+int64_t ma_get_step(const ma_ctx *h);       /* t: number of completed steps */
+int64_t ma_num_blocks(const ma_ctx *h);     /* n_b */
+
+/* Sets the step counter (used when importing a saved state). t >= 0. */
+int ma_set_step(ma_ctx *h, int64_t t);
+/* Sets MA_FLAG_* bits (replaces the previous set). */
+int ma_set_flags(ma_ctx *h, uint32_t flags);
+/* Changes the learning rate used by later steps (finite). */
+int ma_set_lr(ma_ctx *h, float lr);
+
+/*
+ * Copies nbytes at byte_offset of state buffer `which` (MA_STATE_*) to or from
+ * host memory.  Synchronous (waits for the device first).  MA_EINVAL when the
+ * range is outside the buffer (codes: ceil(d/2) bytes, stats: 8*n_b, window:
+ * 4*m*k) or a pointer is NULL.  Together with ma_set_step this exports and
+ * imports the complete state: the random numbers are keyed on (seed, step,
+ * element) and carry no hidden state.
+ */
+int ma_read_state(const ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, void *host_dst);
+int ma_write_state(ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, const void *host_src);
+
+/*
+ * m_hat and v_hat of the last completed step (AdamStats of the first
+ * paragraph, bias-corrected) for nblocks chosen blocks.  blocks: host array of
+ * block numbers.  mhat_out, vhat_out: device f32[nblocks * B_d]; row q holds
+ * block blocks[q], its first len_j entries valid (0 where the window has no
+ * entry).  Enqueued on `stream`.  MA_EINVAL before the first step or for a
+ * block number out of range.
+ */
+int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *mhat_out,
+                     float *vhat_out, hipStream_t stream);
+
+/*
+ * Per-kernel timing with HIP events recorded on the step's stream around each
+ * kernel.  ma_set_timing(h, 1) clears and starts collecting; ma_kernel_times
+ * waits for the recorded events and returns, for nk <= 2 kernels (0: compress,
+ * 1: adamstats_apply), the summed milliseconds and launch counts.
+ */
+int ma_set_timing(ma_ctx *h, int on);
+int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk);
+
+/* Number of parameters the last step's update touched (positions present in
+ * the window), summed over blocks, when counting is enabled by
+ * ma_set_count_touched(h, 1); synchronous read.  -1 when disabled. */
+int ma_set_count_touched(ma_ctx *h, int on);
+int64_t ma_touched_last_step(ma_ctx *h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,154 @@
+"""Python handle over libmicroadam: one MicroAdam optimizer for a flat fp32
+parameter vector on the GPU.  PyTorch supplies device memory and the stream;
+the step itself runs in the library's HIP kernels."""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import _lib as _L
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class MicroAdam:
+    """MicroAdam (page "MicroAdam (Sparse-Gradient Adaptive Optimization with
+    Quantized Error Feedback)") over a flat parameter vector of length d.
+
+    step(params, grads): params is a contiguous fp32 CUDA tensor of d elements,
+    updated in place; grads a contiguous bfloat16 (or int16/uint16 bit
+    pattern) CUDA tensor of d elements.
+    """
+
+    def __init__(self, d: int, block: int = 16384, k: int | None = None, m: int = 10, b: int = 4,
+                 beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, lr: float = 1e-4,
+                 wd: float = 0.0, seed: int = 42):
+        self.d = int(d)
+        self.block = int(block)
+        self.k = int(d // 100 if k is None else k)
+        self.m = int(m)
+        self.b = int(b)
+        self.beta1, self.beta2, self.eps, self.lr, self.wd = beta1, beta2, eps, lr, wd
+        self.seed = int(seed)
+        L = _L.lib()
+        h = L.ma_create(self.d, self.block, self.k, self.m, self.b, beta1, beta2, eps, lr, wd, self.seed)
+        if not h:
+            code, msg = _L.last_error()
+            raise _L.MicroAdamError(code, msg)
+        self._h = C.c_void_p(h)
+
+    # ------------------------------------------------------------ lifecycle
+    def close(self):
+        if getattr(self, "_h", None):
+            _L.lib().ma_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # ------------------------------------------------------------ the step
+    def step(self, params, grads, stream=None):
+        assert params.is_cuda and grads.is_cuda
+        assert params.numel() == self.d and grads.numel() == self.d
+        assert params.is_contiguous() and grads.is_contiguous()
+        assert params.element_size() == 4 and grads.element_size() == 2
+        _L.check(_L.lib().ma_step(self._h, C.c_void_p(params.data_ptr()), C.c_void_p(grads.data_ptr()),
+                                  C.c_void_p(_stream_handle(stream))))
+
+    # ------------------------------------------------------------ accessors
+    @property
+    def t(self) -> int:
+        return int(_L.lib().ma_get_step(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(_L.lib().ma_num_blocks(self._h))
+
+    def state_bytes(self) -> int:
+        return int(_L.lib().ma_state_bytes(self._h))
+
+    def aux_bytes(self) -> int:
+        return int(_L.lib().ma_aux_bytes(self._h))
+
+    def set_flags(self, flags: int):
+        _L.check(_L.lib().ma_set_flags(self._h, int(flags)))
+
+    def set_lr(self, lr: float):
+        _L.check(_L.lib().ma_set_lr(self._h, float(lr)))
+        self.lr = lr
+
+    def set_step(self, t: int):
+        _L.check(_L.lib().ma_set_step(self._h, int(t)))
+
+    def read_state(self, which: int, offset: int, nbytes: int) -> np.ndarray:
+        out = np.empty(int(nbytes), np.uint8)
+        _L.check(_L.lib().ma_read_state(self._h, int(which), int(offset), int(nbytes),
+                                        out.ctypes.data_as(C.c_void_p)))
+        return out
+
+    def write_state(self, which: int, offset: int, data: np.ndarray):
+        data = np.ascontiguousarray(data).view(np.uint8)
+        _L.check(_L.lib().ma_write_state(self._h, int(which), int(offset), data.size,
+                                         data.ctypes.data_as(C.c_void_p)))
+
+    def codes_bytes(self, offset: int = 0, nbytes: int | None = None) -> np.ndarray:
+        n = (self.d + 1) // 2 - offset if nbytes is None else nbytes
+        return self.read_state(_L.MA_STATE_CODES, offset, n)
+
+    def stats(self, first_block: int = 0, nblocks: int | None = None) -> np.ndarray:
+        nb = self.num_blocks - first_block if nblocks is None else nblocks
+        return self.read_state(_L.MA_STATE_STATS, 8 * first_block, 8 * nb).view(np.float32)
+
+    def window(self, offset: int = 0, n: int | None = None) -> np.ndarray:
+        n = self.m * self.k - offset if n is None else n
+        return self.read_state(_L.MA_STATE_WINDOW, 4 * offset, 4 * n).view(np.uint32)
+
+    def export_state(self) -> dict:
+        return {"codes": self.codes_bytes(), "stats": self.stats(), "window": self.window(), "t": self.t}
+
+    def import_state(self, st: dict):
+        self.write_state(_L.MA_STATE_CODES, 0, st["codes"])
+        self.write_state(_L.MA_STATE_STATS, 0, st["stats"])
+        if self.m * self.k:
+            self.write_state(_L.MA_STATE_WINDOW, 0, st["window"])
+        self.set_step(st["t"])
+
+    def moments(self, blocks, stream=None):
+        """(m_hat, v_hat) of the last step for the given blocks, as CUDA
+        tensors of shape [len(blocks), block]."""
+        import torch
+        blocks = np.ascontiguousarray(blocks, dtype=np.int64)
+        mh = torch.empty((blocks.size, self.block), dtype=torch.float32, device="cuda")
+        vh = torch.empty_like(mh)
+        _L.check(_L.lib().ma_debug_moments(self._h, blocks.ctypes.data_as(C.c_void_p), blocks.size,
+                                           C.c_void_p(mh.data_ptr()), C.c_void_p(vh.data_ptr()),
+                                           C.c_void_p(_stream_handle(stream))))
+        return mh, vh
+
+    def set_timing(self, on: bool):
+        _L.check(_L.lib().ma_set_timing(self._h, 1 if on else 0))
+
+    def kernel_times(self):
+        """{'compress': (ms_total, launches), 'adamstats_apply': (...)}"""
+        ms = (C.c_double * 2)()
+        n = (C.c_int64 * 2)()
+        _L.check(_L.lib().ma_kernel_times(self._h, ms, n, 2))
+        return {"compress": (ms[0], n[0]), "adamstats_apply": (ms[1], n[1])}
+
+    def set_count_touched(self, on: bool):
+        _L.check(_L.lib().ma_set_count_touched(self._h, 1 if on else 0))
+
+    def touched_last_step(self) -> int:
+        return int(_L.lib().ma_touched_last_step(self._h))

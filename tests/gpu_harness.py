@@ -1,0 +1,169 @@
+"""Shared helpers for the GPU parity tests: run the HIP library and the CPU
+oracle on the same seeded inputs and compare them element by element.
+
+Bars (from the step's definition): Top-k indices, packed 4-bit codes, block
+statistics and the window contents bit-exact; m_hat, v_hat and the updated
+parameters within 1e-6 relative (|gpu - cpu| <= 1e-6 * max(|cpu|, 1e-30)),
+with the bitwise-equal count reported as well."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from memory_compressed_adaptive_amd import MicroAdam
+from memory_compressed_adaptive_amd import _lib as L
+from memory_compressed_adaptive_amd import synth
+
+REL_TOL = 1e-6
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gauss_grads(rng, d, t, scale=1e-3, outlier=0.01):
+    g = (rng.standard_normal(d) * scale).astype(np.float32)
+    g[rng.random(d) < outlier] *= 50
+    return O.bf16_rne(g)
+
+
+def assert_bits_equal(name, got, ref):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} != {ref.shape}"
+    bad = np.flatnonzero(got.view(np.uint8) != ref.view(np.uint8)) if got.dtype != ref.dtype else \
+        np.flatnonzero(got != ref)
+    if bad.size:
+        i = int(bad[0])
+        raise AssertionError(f"{name}: {bad.size} mismatches, first at {i}: gpu={got.ravel()[i]!r} "
+                             f"cpu={ref.ravel()[i]!r}")
+
+
+def assert_close_f32(name, got, ref):
+    got = np.asarray(got, np.float32)
+    ref = np.asarray(ref, np.float32)
+    same = got.view(np.uint32) == ref.view(np.uint32)
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    tol = REL_TOL * np.maximum(np.abs(ref.astype(np.float64)), 1e-30)
+    ok = same | (err <= tol)
+    if not ok.all():
+        i = int(np.flatnonzero(~ok)[0])
+        raise AssertionError(f"{name}: {int((~ok).sum())} outside 1e-6 rel, first at {i}: "
+                             f"gpu={got[i]!r} cpu={ref[i]!r}")
+    return int((~same).sum())
+
+
+def to_gpu_bf16(g_bits: np.ndarray, misalign: bool = False):
+    t = torch.from_numpy(np.ascontiguousarray(g_bits).view(np.int16))
+    if not misalign:
+        return t.cuda()
+    buf = torch.empty(t.numel() + 1, dtype=torch.int16, device="cuda")
+    buf[1:].copy_(t.cuda())
+    return buf[1:]
+
+
+def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0.999, eps=1e-8,
+                seed=42, flags=0, grad_fn=None, rng_seed=0, moments=True, misalign=False,
+                gpu_only_flags=0):
+    """Full-state comparison after every step.  Returns the optimizer's exported
+    state and the final parameters for further checks."""
+    rng = np.random.default_rng(rng_seed)
+    grad_fn = grad_fn or gauss_grads
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    opt = MicroAdam(d, B, k, m, beta1=beta1, beta2=beta2, eps=eps, lr=lr, wd=wd, seed=seed)
+    opt.set_flags(flags | gpu_only_flags)
+    cfg = O.make_cfg(d, B, k, m, 4, beta1, beta2, eps, lr, wd, seed, flags & O.FLAG_NO_EF)
+    orc = O.FullState(cfg)
+    assert opt.state_bytes() == O.state_bytes(cfg)
+    theta_gpu = torch.from_numpy(theta0.copy()).cuda()
+    theta_cpu = theta0.copy()
+    nb = opt.num_blocks
+    mblocks = np.unique(np.array([0, nb // 2, nb - 1], np.int64))
+    nonbitwise = 0
+    for t in range(1, steps + 1):
+        g = grad_fn(rng, d, t)
+        g_gpu = to_gpu_bf16(g, misalign)
+        say(f"[{label}] step {t}: d={d} B={B} k={k} m={m} wd={wd} flags={flags | gpu_only_flags} "
+            f"misalign={misalign}")
+        opt.step(theta_gpu, g_gpu)
+        torch.cuda.synchronize()
+        mh, vh = orc.step(theta_cpu, g, moments=True)
+        assert opt.t == orc.t == t
+        assert_bits_equal(f"{label} t={t} window", opt.window(), orc.G)
+        assert_bits_equal(f"{label} t={t} codes", opt.codes_bytes(), orc.ef)
+        assert_bits_equal(f"{label} t={t} stats", opt.stats().view(np.uint32), orc.stats.view(np.uint32))
+        nonbitwise += assert_close_f32(f"{label} t={t} theta", theta_gpu.cpu().numpy(), theta_cpu)
+        if moments:
+            gm, gv = opt.moments(mblocks)
+            gm, gv = gm.cpu().numpy(), gv.cpu().numpy()
+            for q, j in enumerate(mblocks):
+                s, n = O.block_range(cfg, int(j))
+                nonbitwise += assert_close_f32(f"{label} t={t} m_hat[{j}]", gm[q, :n], mh[s:s + n])
+                nonbitwise += assert_close_f32(f"{label} t={t} v_hat[{j}]", gv[q, :n], vh[s:s + n])
+    return opt, theta_gpu, theta_cpu, nonbitwise
+
+
+def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_moments=True):
+    """Full-size run on the GPU; the oracle follows a deterministic block
+    sample (every `every`-th block plus the first and last) exactly, since the
+    blocks are independent."""
+    w = workload
+    d, B, k = w.d, w.block, w.k
+    theta = torch.empty(d, dtype=torch.float32, device="cuda")
+    synth.fill_params(theta)
+    g = torch.empty(d, dtype=torch.int16, device="cuda")
+    src = synth.GradSource(w)
+    opt = MicroAdam(d, B, k, m)
+    cfg = O.make_cfg(d, B, k, m)
+    nb = opt.num_blocks
+    blocks = synth.sample_blocks(nb, every)
+    ranges = [O.block_range(cfg, int(j)) for j in blocks]
+    idx = torch.from_numpy(np.concatenate([np.arange(s, s + n) for s, n in ranges])).cuda()
+    torch.cuda.synchronize()
+    th_all = theta.index_select(0, idx).cpu().numpy()
+    states, thetas, pos = {}, {}, 0
+    for j, (s, n) in zip(blocks, ranges):
+        states[int(j)] = O.BlockState.zeros(cfg, int(j))
+        thetas[int(j)] = th_all[pos:pos + n].copy()
+        pos += n
+    nonbitwise = 0
+    for t in range(1, steps + 1):
+        say(f"[{label}] step {t}: {w.name} d={d} m={m} sampled blocks={len(blocks)}")
+        src.fill(g, t)
+        torch.cuda.synchronize()
+        g_all = g.index_select(0, idx).cpu().numpy().view(np.uint16)
+        opt.step(theta, g)
+        torch.cuda.synchronize()
+        th_gpu = theta.index_select(0, idx).cpu().numpy()
+        stats = opt.stats()
+        mh_gpu = vh_gpu = None
+        if check_moments:
+            mg, vg = opt.moments(blocks)
+            mh_gpu, vh_gpu = mg.cpu().numpy(), vg.cpu().numpy()
+        pos = 0
+        for q, (j, (s, n)) in enumerate(zip(blocks, ranges)):
+            j = int(j)
+            bs = states[j]
+            mh, vh = bs.step(thetas[j], g_all[pos:pos + n], moments=True)
+            nonbitwise += assert_close_f32(f"{label} t={t} theta[{j}]", th_gpu[pos:pos + n], thetas[j])
+            pos += n
+            off, kb = O.block_quota(cfg, j)
+            for i in range(m):
+                assert_bits_equal(f"{label} t={t} window row {i} block {j}",
+                                  opt.window(i * k + off, kb), bs.gseg[i])
+            nib0 = s & 1
+            b0 = s >> 1
+            nbytes = (nib0 + n + 1) // 2
+            gcodes = O.unpack_nibbles(opt.codes_bytes(b0, nbytes), n, nib0)
+            assert_bits_equal(f"{label} t={t} codes block {j}", gcodes, bs.codes())
+            assert_bits_equal(f"{label} t={t} stats block {j}", stats[2 * j:2 * j + 2].view(np.uint32),
+                              bs.stats.view(np.uint32))
+            if check_moments:
+                nonbitwise += assert_close_f32(f"{label} t={t} m_hat[{j}]", mh_gpu[q, :n], mh)
+                nonbitwise += assert_close_f32(f"{label} t={t} v_hat[{j}]", vh_gpu[q, :n], vh)
+    del opt
+    return nonbitwise

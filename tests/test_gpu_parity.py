@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element, on the
+same seeded inputs.  Covers the tiny workload in full, ragged and degenerate
+shapes, every kernel variant (chunk counts, aligned and unaligned, sparse and
+dense update, the general selection path, multi-pass slot allocation), and
+full-size workloads on deterministic block samples."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from memory_compressed_adaptive_amd import MicroAdam
+from memory_compressed_adaptive_amd import _lib as L
+from memory_compressed_adaptive_amd import synth
+
+from gpu_harness import (assert_bits_equal, assert_close_f32, full_parity, gauss_grads,
+                         sampled_parity, say, to_gpu_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_tiny_workload_full_state_20_steps():
+    w = synth.WORKLOADS["tiny"]
+    full_parity("tiny", w.d, w.block, w.k, w.m, w.steps)
+
+
+@pytest.mark.parametrize("d,B,k,m,steps", [
+    (100_003, 16384, 1000, 3, 6),     # ragged last block (1699 elements)
+    (20_011, 1003, 500, 4, 5),        # B odd: code bytes straddle blocks, unaligned path
+    (1000, 64, 100, 2, 5),            # tiny blocks
+    (1, 1, 1, 1, 3),                  # a single parameter
+    (7, 3, 2, 2, 4),                  # every block partial
+    (50_000, 4096, 500, 5, 4),        # one chunk per thread
+    (50_000, 8192, 500, 5, 4),        # two chunks per thread
+    (100_000, 32766, 1000, 3, 4),     # eight chunks per thread, largest B_d
+])
+def test_ragged_and_small_shapes(d, B, k, m, steps):
+    full_parity(f"shape d={d} B={B}", d, B, k, m, steps)
+
+
+def test_k_zero_only_error_feedback():
+    full_parity("k=0", 40_000, 4096, 0, 3, 4)
+
+
+def test_k_equals_d_selects_everything():
+    full_parity("k=d", 5_000, 1024, 5_000, 2, 3)
+
+
+def test_general_selection_path_large_quota():
+    # k_b ~ 1638 > 512: the workgroup-wide bit search
+    full_parity("k=d/10", 100_000, 16384, 10_000, 3, 4)
+
+
+def test_ties_constant_and_few_values():
+    def const(rng, d, t):
+        return O.bf16_rne(np.full(d, 1e-3 * t, np.float32))
+
+    def few(rng, d, t):
+        vals = np.array([0.0, 1e-3, -1e-3, 2e-3, -2e-3], np.float32)
+        return O.bf16_rne(vals[rng.integers(0, vals.size, d)])
+
+    full_parity("const grads", 60_000, 16384, 600, 3, 4, grad_fn=const)
+    full_parity("few values", 60_000, 16384, 600, 3, 4, grad_fn=few)
+
+
+def test_all_zero_gradients():
+    full_parity("zero grads", 30_000, 8192, 300, 3, 3, grad_fn=lambda r, d, t: np.zeros(d, np.uint16))
+
+
+def test_m1_no_error_feedback_closed_form():
+    d, B, k = 50_000, 16384, 500
+    opt, theta_gpu, theta_cpu, _ = full_parity("m=1 no-EF", d, B, k, 1, 4, flags=L.MA_FLAG_NO_EF)
+    # the closed form on the GPU's own window: m_hat = c1 V, v_hat = c2 V^2
+    cfg = O.make_cfg(d, B, k, 1)
+    _, _, c1, c2, _ = O.step_constants(cfg, opt.t)
+    G = opt.window()
+    mh, vh = opt.moments(np.arange(opt.num_blocks))
+    mh, vh = mh.cpu().numpy(), vh.cpu().numpy()
+    for j in range(opt.num_blocks):
+        off, kb = O.block_quota(cfg, j)
+        e = G[off:off + kb]
+        I = (e & 0xffff).astype(np.int64)
+        V = O.bf16_to_f32((e >> 16).astype(np.uint16))
+        np.testing.assert_array_equal(mh[j, I], c1 * V)
+        np.testing.assert_array_equal(vh[j, I], c2 * (V * V))
+
+
+def test_weight_decay_dense_update():
+    full_parity("wd dense", 70_000, 16384, 700, 4, 5, lr=1e-2, wd=0.1)
+
+
+def test_forced_dense_equals_sparse():
+    full_parity("force dense", 70_000, 16384, 700, 4, 5, gpu_only_flags=L.MA_FLAG_FORCE_DENSE)
+
+
+def test_misaligned_gradient_pointer():
+    full_parity("misaligned grads", 70_000, 16384, 700, 3, 4, misalign=True)
+
+
+def test_long_window_multi_pass_slots():
+    # m * k_b > LDS slots: the update kernel runs several slot passes
+    full_parity("m=37 k=d/10", 40_000, 16384, 4_000, 37, 40, moments=True)
+
+
+def test_run_twice_is_bitwise_deterministic():
+    runs = []
+    for _ in range(2):
+        opt, theta_gpu, _, _ = full_parity("determinism", 60_000, 16384, 600, 4, 6, rng_seed=3,
+                                           moments=False)
+        runs.append((theta_gpu.cpu().numpy(), opt.export_state()))
+    np.testing.assert_array_equal(runs[0][0].view(np.uint32), runs[1][0].view(np.uint32))
+    for key in ("codes", "stats", "window"):
+        np.testing.assert_array_equal(np.asarray(runs[0][1][key]).view(np.uint8),
+                                      np.asarray(runs[1][1][key]).view(np.uint8))
+
+
+def test_export_import_resume():
+    d, B, k, m = 60_000, 16384, 600, 4
+    rng = np.random.default_rng(9)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    grads = [gauss_grads(rng, d, t) for t in range(1, 9)]
+    a = MicroAdam(d, B, k, m)
+    ta = torch.from_numpy(theta0.copy()).cuda()
+    for t in range(4):
+        a.step(ta, to_gpu_bf16(grads[t]))
+    torch.cuda.synchronize()
+    st = a.export_state()
+    tb = ta.clone()
+    b = MicroAdam(d, B, k, m)
+    b.import_state(st)
+    say("[resume] continuing both runs for 4 steps")
+    for t in range(4, 8):
+        a.step(ta, to_gpu_bf16(grads[t]))
+        b.step(tb, to_gpu_bf16(grads[t]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ta.cpu().numpy().view(np.uint32), tb.cpu().numpy().view(np.uint32))
+    sa, sb = a.export_state(), b.export_state()
+    for key in ("codes", "stats", "window"):
+        np.testing.assert_array_equal(np.asarray(sa[key]).view(np.uint8), np.asarray(sb[key]).view(np.uint8))
+
+
+def test_update_sparsity_on_gpu():
+    # at most |union of window rows| <= m*k parameters change per step
+    w = synth.WORKLOADS["tiny"]
+    opt = MicroAdam(w.d, w.block, w.k, w.m)
+    opt.set_count_touched(True)
+    theta = torch.empty(w.d, dtype=torch.float32, device="cuda")
+    synth.fill_params(theta)
+    g = torch.empty(w.d, dtype=torch.int16, device="cuda")
+    src = synth.GradSource(w)
+    for t in range(1, 16):
+        src.fill(g, t)
+        before = theta.clone()
+        opt.step(theta, g)
+        torch.cuda.synchronize()
+        changed = int((theta.view(torch.int32) != before.view(torch.int32)).sum())
+        touched = opt.touched_last_step()
+        assert changed <= touched <= min(t, w.m) * w.k
+        assert 1 - changed / w.d >= 1 - w.m * w.k / w.d >= 0.9 - 1e-3
+
+
+def test_error_codes_on_gpu_handle():
+    opt = MicroAdam(1000, 100, 10, 2)
+    theta = torch.zeros(1000, dtype=torch.float32, device="cuda")
+    g = torch.zeros(1000, dtype=torch.int16, device="cuda")
+    lib = L.lib()
+    import ctypes as C
+    assert lib.ma_step(opt.handle, None, C.c_void_p(g.data_ptr()), None) == L.MA_EINVAL
+    assert lib.ma_step(opt.handle, C.c_void_p(theta.data_ptr() + 2), C.c_void_p(g.data_ptr()), None) == L.MA_EINVAL
+    assert opt.t == 0
+    assert lib.ma_read_state(opt.handle, L.MA_STATE_CODES, 0, 10_000, C.c_void_p(1)) == L.MA_EINVAL
+    buf = (C.c_uint8 * 8)()
+    assert lib.ma_debug_moments(opt.handle, buf, 1, C.c_void_p(1), C.c_void_p(1), None) == L.MA_EINVAL
+    opt.step(theta, g)
+    torch.cuda.synchronize()
+    assert opt.t == 1
+
+
+def test_create_destroy_does_not_leak():
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(30):
+        o = MicroAdam(5_000_000, 16384, 50_000, 10)
+        o.close()
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 - free1 < 64 << 20
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled blocks
+
+def test_bert_base_sampled():
+    sampled_parity("bert_base", synth.WORKLOADS["bert_base"], 10, 4, every=97)
+
+
+def test_opt_1_3b_sampled():
+    sampled_parity("opt_1_3b", synth.WORKLOADS["opt_1_3b"], 10, 3, every=397)
+
+
+def test_llama2_7b_sampled():
+    sampled_parity("llama2_7b", synth.WORKLOADS["llama2_7b"], 10, 3, every=997)
+
+
+@pytest.mark.parametrize("m", [1, 10, 20, 37])
+def test_llama2_13b_sampled_window_sweep(m):
+    sampled_parity(f"llama2_13b m={m}", synth.WORKLOADS["llama2_13b"], m, 2, every=3989,
+                   check_moments=(m == 37))
