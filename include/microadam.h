@@ -146,11 +146,13 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
 int ma_set_timing(ma_ctx *h, int on);
 int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk);
 
-/* Number of parameters the last step's update touched (positions present in
- * the window), summed over blocks, when counting is enabled by
- * ma_set_count_touched(h, 1); synchronous read.  -1 when disabled. */
+/* Counting of touched parameters (positions present in the window, i.e. the
+ * parameters an update reads and writes), summed over blocks and steps.
+ * ma_set_count_touched(h, 1) zeroes the counter (synchronous) and makes every
+ * later step add its count on the device; ma_touched_count waits for the
+ * device and returns the sum, or -1 when counting is off. */
 int ma_set_count_touched(ma_ctx *h, int on);
-int64_t ma_touched_last_step(ma_ctx *h);
+int64_t ma_touched_count(ma_ctx *h);
 
 #ifdef __cplusplus
 }

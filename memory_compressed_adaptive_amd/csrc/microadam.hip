@@ -355,7 +355,6 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     }
     hipEventRecord(ev.e[0], stream);
   }
-  if (h->count_touched) hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, h->touched);
   hipError_t e = dispatch_compress(h->cpt, g_al, ca, h->n_b, stream);
   if (e == hipSuccess && h->timing) hipEventRecord(ev.e[1], stream);
   if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream);
@@ -476,18 +475,23 @@ int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk) {
 int ma_set_count_touched(ma_ctx *h, int on) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_count_touched: null handle");
+  DeviceGuard guard(h->device);
+  if (on && (hipDeviceSynchronize() != hipSuccess ||
+             hipMemset(h->touched, 0, sizeof(unsigned long long)) != hipSuccess ||
+             hipDeviceSynchronize() != hipSuccess))
+    return fail(MA_EHIP, "ma_set_count_touched: clearing the counter failed");
   h->count_touched = on != 0;
   return MA_OK;
 }
 
-int64_t ma_touched_last_step(ma_ctx *h) {
+int64_t ma_touched_count(ma_ctx *h) {
   clear_error();
   if (!h || !h->count_touched) return -1;
   DeviceGuard guard(h->device);
   unsigned long long v = 0;
   if (hipDeviceSynchronize() != hipSuccess ||
       hipMemcpy(&v, h->touched, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) {
-    fail(MA_EHIP, "ma_touched_last_step: copy failed");
+    fail(MA_EHIP, "ma_touched_count: copy failed");
     return -1;
   }
   return (int64_t)v;

@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
   if (use_ef) {
     lo = A.stats[2 * j];
     const float hi = A.stats[2 * j + 1];
-    step = __fdiv_rn(hi - lo, 15.0f);
+    step = (hi - lo) / 15.0f;
   }
   float a[CPT][kChunk];
   uint32_t oldc[CPT];
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
 
   // ---------------- ef_requant: unbiased stochastic 4-bit rounding
   const bool flat = (mx == mn);
-  const float inv = flat ? 0.f : __fdiv_rn(15.0f, mx - mn);
+  const float inv = flat ? 0.f : 15.0f / (mx - mn);
   const uint32_t bkey = philox_block_key(A.seed, A.t, j);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
         const float mh = A.c1 * s_z1[x];
         const float vh = A.c2 * s_z2[x];
         float *tp = A.theta + s + p;
-        const float upd = A.lr * __fdiv_rn(mh, __fsqrt_rn(vh) + A.eps);
+        const float upd = A.lr * (mh / (sqrtf(vh) + A.eps));
         *tp = *tp - upd;
       }
     } else {
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
                 const float mh = A.c1 * s_z1[sl];
                 const float vh = A.c2 * s_z2[sl];
                 if (MODE == kModeDense) {
-                  th[c][e] = th[c][e] - A.lr * __fdiv_rn(mh, __fsqrt_rn(vh) + A.eps);
+                  th[c][e] = th[c][e] - A.lr * (mh / (sqrtf(vh) + A.eps));
                 } else {
                   A.mhat[(int64_t)blockIdx.x * A.B + i] = mh;
                   A.vhat[(int64_t)blockIdx.x * A.B + i] = vh;
@@ -749,7 +749,5 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
     }
   }
 }
-
-__global__ void zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
 
 }  // namespace microadam

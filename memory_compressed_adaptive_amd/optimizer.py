@@ -150,5 +150,6 @@ class MicroAdam:
     def set_count_touched(self, on: bool):
         _L.check(_L.lib().ma_set_count_touched(self._h, 1 if on else 0))
 
-    def touched_last_step(self) -> int:
-        return int(_L.lib().ma_touched_last_step(self._h))
+    def touched_count(self) -> int:
+        """Touched parameters summed over the steps since set_count_touched(True)."""
+        return int(_L.lib().ma_touched_count(self._h))
