@@ -1,0 +1,260 @@
+"""Benchmark: MicroAdam optimizer steps/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama2_7b] [--m 10]
+
+A step is one full MicroAdam step (accumulate the 4-bit error, block Top-k,
+requantize, window write, AdamStats and the AdamW update) over the whole flat
+parameter vector of the workload (default: the LLaMA-2-7B-shaped set, m = 10,
+k = d/100, B_d = 16384), with parameters, gradients and optimizer state
+resident in HBM before the timed region.  Gradients come from a pool of
+pre-generated seeded synthetic steps, cycled.
+
+Prints ONE JSON line with steps/s (value), the dominant kernel's roofline
+(algorithmic bytes per launch / its average HIP-event duration, against
+8 TB/s), the CPU oracle timed on a bounded block sample of the same workload
+(cpu_baseline) and the oracle-vs-GPU check of those sampled blocks after the
+run (parity_sampled).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MicroAdam optimizer steps/s at LLaMA-2-7B shape (m=10,k=d/100); HBM GB/s vs peak"
+KERNEL_SRC = os.path.join(ROOT, "memory_compressed_adaptive_amd", "csrc", "microadam_kernels.hpp")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str, m: int):
+    """Counter-measured HBM bytes per launch, if a committed summary exists for
+    the current kernel source (null once the kernels have changed)."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_m{m}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--m", type=int, default=None)
+    ap.add_argument("--pool", type=int, default=0,
+                    help="distinct pre-generated gradient steps (default: one per step, as memory allows)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=400, help="blocks in the oracle sample")
+    ap.add_argument("--dense", action="store_true", help="stream all parameters in the update")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the MicroAdam step needs no communication "
+              "(every block is independent); multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from memory_compressed_adaptive_amd import MicroAdam
+    from memory_compressed_adaptive_amd import _lib as L
+    from memory_compressed_adaptive_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    m = args.m or w.m
+    K = args.steps or w.steps
+    W = args.warmup
+    d, B, k = w.d, w.block, w.k
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload={w.name} d={d} B_d={B} k={k} m={m} steps={K} warmup={W}")
+
+    # ---------------- HBM copy ceiling (plain streaming copy, same process)
+    n_copy = 1 << 30
+    src = torch.empty(n_copy, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    synth.copy_f32(dst, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        synth.copy_f32(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * 4 * n_copy / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"copy kernel: {copy_gbps:.0f} GB/s")
+
+    # ---------------- inputs resident in HBM
+    theta = torch.empty(d, dtype=torch.float32, device=dev)
+    synth.fill_params(theta)
+    gsrc = synth.GradSource(w)
+    free, _ = torch.cuda.mem_get_info()
+    state_est = (d + 1) // 2 + 4 * m * k + 64 * (d // B + 1)
+    fit = int((free - state_est - (8 << 30)) // (2 * d))
+    P = max(1, min(args.pool or (K + W), K + W, fit))
+    pool = []
+    for p in range(P):
+        g = torch.empty(d, dtype=torch.int16, device=dev)
+        gsrc.fill(g, p + 1)
+        pool.append(g)
+    torch.cuda.synchronize()
+    log(f"inputs ready: theta {4 * d / 2**30:.1f} GiB, {P} gradient steps {2 * d * P / 2**30:.1f} GiB")
+
+    opt = MicroAdam(d, B, k, m)
+    if args.dense:
+        opt.set_flags(L.MA_FLAG_FORCE_DENSE)
+    nb = opt.num_blocks
+
+    # oracle sample: initial parameters and every pooled gradient of the sampled blocks
+    cpu_leg = not args.no_cpu_baseline
+    if cpu_leg:
+        every = max(1, nb // max(1, args.cpu_blocks))
+        blocks = synth.sample_blocks(nb, every)
+        ranges = [(int(j) * B, min(B, d - int(j) * B)) for j in blocks]
+        idx = torch.from_numpy(np.concatenate([np.arange(s, s + n) for s, n in ranges])).to(dev)
+        th0 = theta.index_select(0, idx).cpu().numpy()
+        g_host = [g.index_select(0, idx).cpu().numpy().view(np.uint16) for g in pool]
+
+    # ---------------- warmup, then exactly K timed steps
+    for s in range(W):
+        opt.step(theta, pool[s % P])
+    torch.cuda.synchronize()
+    opt.set_timing(True)
+    opt.set_count_touched(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(W, W + K):
+        opt.step(theta, pool[s % P])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    kt = opt.kernel_times()
+    touched = opt.touched_count() / K
+    opt.set_count_touched(False)
+    opt.set_timing(False)
+    steps_per_s = K / elapsed
+    log(f"{K} steps in {elapsed * 1e3:.2f} ms: {steps_per_s:.2f} steps/s")
+
+    # ---------------- roofline of the dominant kernel
+    ms_c = kt["compress"][0] / max(1, kt["compress"][1])
+    ms_a = kt["adamstats_apply"][0] / max(1, kt["adamstats_apply"][1])
+    bytes_c = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb       # g, codes r+w, window row, stats r+w
+    bytes_a = 4 * m * k + 8 * touched                           # window read, touched theta r+w
+    kern = {"compress": (ms_c, bytes_c), "adamstats_apply": (ms_a, bytes_a)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    ms_dom, bytes_dom = kern[dom]
+    achieved = bytes_dom / (ms_dom * 1e-3) / 1e9
+    traffic = load_traffic(w.name, m)
+    traffic_bytes = None
+    if traffic is not None and dom in traffic.get("kernels", {}):
+        kt_ = traffic["kernels"][dom]
+        traffic_bytes = kt_["fetch_bytes"] + kt_["write_bytes"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes,
+                "bytes_per_launch": int(bytes_dom), "avg_launch_ms": round(ms_dom, 4)}
+    step_bytes = bytes_c + bytes_a
+    hbm = {"algorithmic_GB_per_step": round(step_bytes / 1e9, 3),
+           "algorithmic_GBps": round(step_bytes * steps_per_s / 1e9, 1),
+           "copy_kernel_GBps": round(copy_gbps, 1),
+           "touched_fraction": round(touched / d, 5),
+           "kernels_ms": {"compress": round(ms_c, 4), "adamstats_apply": round(ms_a, 4)},
+           "kernels_algorithmic_GBps": {n: round(kern[n][1] / (kern[n][0] * 1e-3) / 1e9, 1) for n in kern}}
+    if traffic is not None:
+        tot = sum(v["fetch_bytes"] + v["write_bytes"] for v in traffic["kernels"].values())
+        hbm["counter_GB_per_step"] = round(tot / 1e9, 3)
+        hbm["counter_GBps"] = round(tot / ((ms_c + ms_a) * 1e-3) / 1e9, 1)
+
+    result = {
+        "metric": METRIC, "value": round(steps_per_s, 3), "unit": "steps/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "d": d, "B_d": B, "k": k, "m": m, "b": 4,
+                   "grad_pool": P, "update": "dense" if args.dense else "sparse"},
+        "params_per_s": round(d * steps_per_s, 1),
+        "state_bytes": opt.state_bytes(),
+        "hbm": hbm,
+        "roofline": roofline,
+    }
+
+    # ---------------- CPU baseline: the oracle on the sampled blocks, same inputs
+    if cpu_leg:
+        import oracle as O
+        log(f"oracle on {len(blocks)} sampled blocks x {W + K} steps ...")
+        th_gpu = theta.index_select(0, idx).cpu().numpy()
+        stats_gpu = opt.stats()
+        cfg = O.make_cfg(d, B, k, m)
+        states = {int(j): O.BlockState.zeros(cfg, int(j)) for j in blocks}
+        ths = []
+        pos = 0
+        for (s, n) in ranges:
+            ths.append(th0[pos:pos + n].copy())
+            pos += n
+        c0 = time.perf_counter()
+        for s in range(W + K):
+            gh = g_host[s % P]
+            pos = 0
+            for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
+                states[int(j)].step(ths[q], gh[pos:pos + n])
+                pos += n
+        c1 = time.perf_counter()
+        per_block_step = (c1 - c0) / (len(blocks) * (W + K))
+        cpu_steps_per_s = 1.0 / (per_block_step * nb)
+        result["cpu_baseline"] = {
+            "value": round(cpu_steps_per_s, 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(blocks)} of {nb} blocks (every {every}th, plus first and last) x {W + K} steps "
+                      f"of {w.name}; {c1 - c0:.1f} s single-threaded, extrapolated to all blocks",
+            "host_cpus": os.cpu_count()}
+        # parity of the sampled blocks after the whole run
+        bad = {"theta": 0, "codes": 0, "stats": 0, "window": 0}
+        nonbitwise = 0
+        pos = 0
+        for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
+            j = int(j)
+            bs = states[j]
+            got = th_gpu[pos:pos + n]
+            ref = ths[q]
+            pos += n
+            same = got.view(np.uint32) == ref.view(np.uint32)
+            close = np.abs(got.astype(np.float64) - ref) <= 1e-6 * np.maximum(np.abs(ref), 1e-30)
+            bad["theta"] += int((~(same | close)).sum())
+            nonbitwise += int((~same).sum())
+            codes = O.unpack_nibbles(opt.codes_bytes(s0 >> 1, ((s0 & 1) + n + 1) // 2), n, s0 & 1)
+            bad["codes"] += int((codes != bs.codes()).sum())
+            bad["stats"] += int((stats_gpu[2 * j:2 * j + 2].view(np.uint32) != bs.stats.view(np.uint32)).sum())
+            off, kb = O.block_quota(cfg, j)
+            for i in range(m):
+                bad["window"] += int((opt.window(i * k + off, kb) != bs.gseg[i]).sum())
+        result["parity_sampled"] = {"blocks": len(blocks), "steps": W + K, "ok": not any(bad.values()),
+                                    "mismatches": bad, "theta_not_bitwise": nonbitwise}
+        log(f"cpu baseline {cpu_steps_per_s:.5f} steps/s (extrapolated); parity ok={result['parity_sampled']['ok']}")
+
+    opt.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,7 @@ struct ma_ctx {
   int device = 0;
   int cpt = 1;       // 4096-element chunks per thread
   int cap = 0;       // LDS slots per pass of the update kernel
+  int ent_cap = 0;   // window entries of one block the update kernel keeps in LDS
   size_t apply_lds = 0;
 
   uint8_t *codes = nullptr;
@@ -108,23 +109,35 @@ struct DeviceGuard {
   }
 };
 
-template <int CPT, bool AL>
-hipError_t launch_compress(const CompressArgs &a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((compress_kernel<CPT, AL>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+template <int CPT, bool AL, bool EF>
+hipError_t launch_compress(const CompressArgs &a, int64_t n_full, int64_t n_b, hipStream_t s) {
+  if (CPT <= 4 && AL && n_full > 0)
+    hipLaunchKernelGGL((compress_full_kernel<(CPT <= 4 ? CPT : 4), EF>), dim3((unsigned)n_full), dim3(kThreads), 0,
+                       s, a);
+  if (n_b > n_full)
+    hipLaunchKernelGGL((compress_kernel<CPT, AL, EF>), dim3((unsigned)(n_b - n_full)), dim3(kThreads), 0, s, a,
+                       n_full);
   return hipGetLastError();
 }
 
 template <int CPT>
-hipError_t launch_compress_cpt(bool aligned, const CompressArgs &a, int64_t grid, hipStream_t s) {
-  return aligned ? launch_compress<CPT, true>(a, grid, s) : launch_compress<CPT, false>(a, grid, s);
+hipError_t launch_compress_cpt(bool aligned, bool ef, const CompressArgs &a, int64_t n_full, int64_t n_b,
+                               hipStream_t s) {
+  if (ef)
+    return aligned ? launch_compress<CPT, true, true>(a, n_full, n_b, s)
+                   : launch_compress<CPT, false, true>(a, n_full, n_b, s);
+  return aligned ? launch_compress<CPT, true, false>(a, n_full, n_b, s)
+                 : launch_compress<CPT, false, false>(a, n_full, n_b, s);
 }
 
-hipError_t dispatch_compress(int cpt, bool aligned, const CompressArgs &a, int64_t grid, hipStream_t s) {
+// Blocks 0 .. n_full-1 take the bounds-free kernel; the rest the general one.
+hipError_t dispatch_compress(int cpt, bool aligned, bool ef, const CompressArgs &a, int64_t n_full, int64_t n_b,
+                             hipStream_t s) {
   switch (cpt) {
-    case 1: return launch_compress_cpt<1>(aligned, a, grid, s);
-    case 2: return launch_compress_cpt<2>(aligned, a, grid, s);
-    case 4: return launch_compress_cpt<4>(aligned, a, grid, s);
-    default: return launch_compress_cpt<8>(aligned, a, grid, s);
+    case 1: return launch_compress_cpt<1>(aligned, ef, a, n_full, n_b, s);
+    case 2: return launch_compress_cpt<2>(aligned, ef, a, n_full, n_b, s);
+    case 4: return launch_compress_cpt<4>(aligned, ef, a, n_full, n_b, s);
+    default: return launch_compress_cpt<8>(aligned, ef, a, 0, n_b, s);
   }
 }
 
@@ -164,6 +177,7 @@ ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float 
   a.m = h->m;
   a.tm = (int32_t)(t % h->m);
   a.cap = h->cap;
+  a.ent_cap = h->ent_cap;
   a.c1 = c1;
   a.c2 = c2;
   a.lr = h->lr;
@@ -220,12 +234,16 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     bp[(size_t)r] = (float)std::pow((double)beta1, (double)r);
     bp[(size_t)m + r] = (float)std::pow((double)beta2, (double)r);
   }
-  // the update kernel's slots: at most min(B_d, m*kb_max) touched positions
+  // The update kernel's LDS: bitmap and slot bases (8 bytes per 32 positions),
+  // the block's window entries when they fit in a quarter of the budget, and
+  // 10 bytes per slot for at most min(B_d, m*kb_max) touched positions.
   const int W = h->cpt * kChunkSpan / 32;
-  const int64_t umax = std::min<int64_t>((int64_t)B_d, (int64_t)m * kb_max);
-  const int64_t cap_limit = ((int64_t)kApplyLdsLimit - 8 * (int64_t)W) / 10;
+  const int64_t ents = (int64_t)m * kb_max;
+  h->ent_cap = (4 * ents <= (int64_t)kApplyLdsLimit / 4) ? (int)ents : 0;
+  const int64_t umax = std::min<int64_t>((int64_t)B_d, ents);
+  const int64_t cap_limit = ((int64_t)kApplyLdsLimit - 8 * (int64_t)W - 4 * (int64_t)h->ent_cap) / 10;
   h->cap = (int)std::max<int64_t>(1, std::min<int64_t>(umax, cap_limit));
-  h->apply_lds = 8 * (size_t)W + 10 * (size_t)h->cap;
+  h->apply_lds = 8 * (size_t)W + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
 
   h->codes_bytes = (size_t)((d + 1) / 2);
   h->codes_alloc = (h->codes_bytes + 15) & ~(size_t)15;
@@ -333,7 +351,6 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   ca.row_base = (t % h->m) * h->k;
   ca.seed = h->seed;
   ca.B = h->B;
-  ca.flags = (h->flags & MA_FLAG_NO_EF) ? kFlagNoEF : 0u;
 
   ApplyArgs aa = make_apply_args(h, t, c1, c2, decay);
   aa.theta = params;
@@ -355,7 +372,8 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     }
     hipEventRecord(ev.e[0], stream);
   }
-  hipError_t e = dispatch_compress(h->cpt, g_al, ca, h->n_b, stream);
+  const int64_t n_full = (g_al && h->B == h->cpt * kChunkSpan) ? h->d / h->B : 0;
+  hipError_t e = dispatch_compress(h->cpt, g_al, !(h->flags & MA_FLAG_NO_EF), ca, n_full, h->n_b, stream);
   if (e == hipSuccess && h->timing) hipEventRecord(ev.e[1], stream);
   if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream);
   if (h->timing) {

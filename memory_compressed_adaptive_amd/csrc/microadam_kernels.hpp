@@ -34,7 +34,6 @@ constexpr int kChunk = 8;                       // consecutive elements per thre
 constexpr int kChunkSpan = kThreads * kChunk;   // 4096 elements per chunk
 constexpr int kCandMax = 512;                   // candidates one wave selects from (8 per lane)
 constexpr int kCoarseLowBit = 16;               // candidate threshold keeps key bits 30..16
-constexpr uint32_t kFlagNoEF = 1u;
 
 // ------------------------------------------------------------------ scalars
 
@@ -42,6 +41,13 @@ __device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return u2f(h << 16); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read exactly once (streamed past the caches)
+__device__ __forceinline__ u32x4 load_stream16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // fp32 -> bfloat16 bits, round to nearest even (the window stores bfloat16
 // values).  Adding 0x7fff plus the kept half's lowest bit carries into the
@@ -90,38 +96,53 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Cross-lane steps use DPP: row_shr:n shifts within 16-lane rows (zero fill
+// at the row start), row_ror:n rotates within rows, row_bcast:15 / :31 carry
+// lane 15 / 31 into the following rows.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v += dpp_u32<0x111, 0xf>(0u, v);   // row_shr:1
+  v += dpp_u32<0x112, 0xf>(0u, v);   // row_shr:2
+  v += dpp_u32<0x114, 0xf>(0u, v);   // row_shr:4
+  v += dpp_u32<0x118, 0xf>(0u, v);   // row_shr:8
+  v += dpp_u32<0x142, 0xa>(0u, v);   // row_bcast:15 into rows 1, 3
+  v += dpp_u32<0x143, 0xc>(0u, v);   // row_bcast:31 into rows 2, 3
   return v;
 }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
 }
 
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
+// min / max over the 64 lanes, returned uniformly (lane 63 ends with the result)
+template <bool MAX>
+__device__ __forceinline__ float wave_minmax(float v) {
+#define MA_STEP(CTRL, RM)                                                            \
+  {                                                                                 \
+    const float o = u2f(dpp_u32<CTRL, RM>(f2u(v), f2u(v)));                         \
+    v = MAX ? fmaxf(v, o) : fminf(v, o);                                            \
+  }
+  MA_STEP(0x121, 0xf)   // row_ror:1
+  MA_STEP(0x122, 0xf)   // row_ror:2
+  MA_STEP(0x124, 0xf)   // row_ror:4
+  MA_STEP(0x128, 0xf)   // row_ror:8
+  MA_STEP(0x142, 0xa)   // row_bcast:15
+  MA_STEP(0x143, 0xc)   // row_bcast:31
+#undef MA_STEP
+  return u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(v), 63));
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+__device__ __forceinline__ float wave_min(float v) { return wave_minmax<false>(v); }
+__device__ __forceinline__ float wave_max(float v) { return wave_minmax<true>(v); }
 
 // Sum over the workgroup (two barriers; s_red holds kWaves words).
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *s_red) {
   v = wave_sum(v);
-  if (lane_id() == 0) s_red[threadIdx.x >> 6] = v;
+  if (lane_id() == 63) s_red[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t tot = 0;
 #pragma unroll
@@ -182,53 +203,79 @@ struct CompressArgs {
   int64_t row_base;         // (t mod m) * k
   uint64_t seed;
   int32_t B;
-  uint32_t flags;
 };
 
-// One block of the compressor.  CPT = 4096-element chunks per thread.
-// ALIGNED: B_d % 8 == 0 and the gradient pointer is 16-byte aligned, so a
-// thread's 8 elements are one 16-byte gradient load and one 4-byte code word.
-template <int CPT, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
-  __shared__ uint32_t s_red[kWaves];
-  __shared__ float s_redf[2 * kWaves];
-  __shared__ uint32_t s_cnt[CPT * kWaves + 1];
-  __shared__ uint32_t s_candA[kCandMax];
-  __shared__ uint16_t s_candI[kCandMax];
-  __shared__ uint32_t s_sel[2];
+template <int CPT>
+struct CompressSmem {
+  uint32_t red[kWaves];
+  float redf[2 * kWaves];
+  uint32_t cnt[CPT * kWaves + 1];
+  uint2 cand[kCandMax];     // {bits of a, index}
+  uint32_t sel[4];          // T, idx_last, exact cut
+};
 
+// Quantization code of one element (the third paragraph's unbiased Q):
+// code = floor(y) + [u < frac(y) * 2^16], capped at 15, with y = (v - lo) * inv
+// and u the element's 16-bit uniform.  With Y = y * 2^16 (exact scaling) and
+// nu = 65535 - u this is (ceil(Y) + nu) >> 16: ceil(Y) = 2^16 floor(y) +
+// ceil(2^16 frac(y)), and ceil(2^16 frac) + 65535 - u >= 2^16 exactly when
+// 2^16 frac > u.
+__device__ __forceinline__ uint32_t quant_code(float v, float lo, float inv, uint32_t nu) {
+  const float y = (v - lo) * inv;
+  const float Y = y * 65536.0f;
+  const uint32_t c = (uint32_t)ceilf(Y);
+  return min((c + nu) >> 16, 15u);
+}
+
+// One block of the compressor, templated on the chunk count (CPT), on whether
+// every element of the thread's chunks exists (FULL: no bounds tests, vector
+// loads), on 16-byte alignment of the gradient / 8-element alignment of the
+// block (ALIGNED: one 16-byte gradient load and one 4-byte code word per
+// thread and chunk) and on error feedback being on (EF).
+template <int CPT, bool FULL, bool ALIGNED, bool EF>
+__device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
+                                               int64_t s, int L, int64_t off, int kb) {
   const int tid = (int)threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const int64_t j = xcd_block((int64_t)blockIdx.x, A.n_b);
-  const int64_t s = j * (int64_t)A.B;
-  const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
-  const int64_t off = A.off_tab[j];
-  const int kb = (int)(A.off_tab[j + 1] - off);
-  const bool use_ef = !(A.flags & kFlagNoEF);
 
-  // ---------------- ef_dequant_accumulate: a = f32(g) + fmaf(code, s, delta)
+  // ---------------- ef_dequant_accumulate: a = f32(g) + fmaf(code, step, delta)
   float lo = 0.f, step = 0.f;
-  if (use_ef) {
+  if (EF) {
     lo = A.stats[2 * j];
     const float hi = A.stats[2 * j + 1];
     step = (hi - lo) / 15.0f;
   }
   float a[CPT][kChunk];
   uint32_t oldc[CPT];
+  if (FULL && ALIGNED) {
+    u32x4 gv[CPT];
+    uint32_t cw[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int i0 = c * kChunkSpan + tid * kChunk;
-    if (ALIGNED && i0 + kChunk <= L) {
-      const uint4 gv = *reinterpret_cast<const uint4 *>(A.g + s + i0);
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-      const uint32_t cw = use_ef ? *reinterpret_cast<const uint32_t *>(A.ef + ((s + i0) >> 1)) : 0u;
-      oldc[c] = cw;
+    for (int c = 0; c < CPT; ++c) {
+      const int i0 = c * kChunkSpan + tid * kChunk;
+      gv[c] = load_stream16(A.g + s + i0);
+      cw[c] = EF ? *reinterpret_cast<const uint32_t *>(A.ef + ((s + i0) >> 1)) : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      oldc[c] = cw[c];
+      const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
+      const uint32_t ce = cw[c] & 0x0f0f0f0fu, co = (cw[c] >> 4) & 0x0f0f0f0fu;
 #pragma unroll
       for (int e = 0; e < kChunk; ++e) {
-        const uint32_t gb = (e & 1) ? (gw[e >> 1] >> 16) : (gw[e >> 1] & 0xffffu);
-        const float gf = bf16_bits_to_f32(gb);
-        a[c][e] = use_ef ? gf + fmaf((float)((cw >> (4 * e)) & 15u), step, lo) : gf;
+        const float gf = (e & 1) ? u2f(gw[e >> 1] & 0xffff0000u) : u2f(gw[e >> 1] << 16);
+        if (EF) {
+          const uint32_t cb = (e & 1) ? co : ce;
+          const float code = (float)((cb >> (8 * (e >> 1))) & 0xffu);
+          a[c][e] = gf + fmaf(code, step, lo);
+        } else {
+          a[c][e] = gf;
+        }
       }
-    } else {
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int i0 = c * kChunkSpan + tid * kChunk;
       uint32_t cw = 0;
 #pragma unroll
       for (int e = 0; e < kChunk; ++e) {
@@ -237,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
         if (i < L) {
           const int64_t gi = s + i;
           const float gf = bf16_bits_to_f32(A.g[gi]);
-          if (use_ef) {
+          if (EF) {
             const uint32_t code = (A.ef[gi >> 1] >> (4 * (int)(gi & 1))) & 15u;
             cw |= code << (4 * e);
             v = gf + fmaf((float)code, step, lo);
@@ -250,80 +297,83 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
       oldc[c] = cw;
     }
   }
+#define MA_VALID(i) (FULL || (i) < L)
 
-  // ---------------- block_topk: the k_b largest |a| (as 31-bit patterns),
-  // ties to the lower index.  Result: threshold key T and the index of the
-  // last selected element with key T; selected <=> key > T or (key == T and
-  // index <= idx_last).
-  uint32_t T = 0xffffffffu;
+  // ---------------- block_topk: the k_b largest |a| (keys = 31-bit patterns),
+  // ties to the lower index.  For finite values the key order is the order of
+  // |a| as floats, so the passes over all elements compare |a| (a free source
+  // modifier) with thresholds given as keys; the inputs must be finite.  Result: threshold key T and idx_last, the index
+  // of the last selected element with key T; an element is selected iff
+  // key > T, or key == T and index <= idx_last.  exact: every element with key
+  // T is selected (then "key >= T" alone decides).
+  uint32_t T = 0x7f800000u;   // k_b = 0: the key of +inf, above every finite |a|
   int idx_last = -1;
+  bool exact = true;
   if (kb > 0) {
     bool done = false;
     const int q = (kb + kWaves - 1) / kWaves;
     if (q <= 64 && kb < L) {
-      // (1) a candidate threshold tau with at least k_b keys >= tau: every wave
-      // finds a value its q-th largest lane maximum reaches; tau is their
-      // minimum, so at least kWaves*q >= k_b distinct elements reach tau.
-      uint32_t lanemax = 0;
+      // (1) candidate threshold tau with at least k_b keys >= tau: each wave
+      // finds a value reached by q of its lane maxima; tau = their minimum, so
+      // at least kWaves * q >= k_b distinct elements reach it.
+      // For finite values the 31-bit key order is the order of |a| as floats,
+      // so the streaming passes compare |a| (a free source modifier) instead of
+      // materialising keys.
+      float lanemax_f = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const int i = c * kChunkSpan + tid * kChunk + e;
-          const uint32_t key = f2u(a[c][e]) & 0x7fffffffu;
-          if (i < L && key > lanemax) lanemax = key;
-        }
+        for (int e = 0; e < kChunk; ++e)
+          if (MA_VALID(c * kChunkSpan + tid * kChunk + e)) lanemax_f = fmaxf(lanemax_f, fabsf(a[c][e]));
+      const uint32_t lanemax = f2u(lanemax_f);
       uint32_t P = 0;
       for (int b = 30; b >= kCoarseLowBit; --b) {
         const uint32_t cand = P | (1u << b);
         if ((int)__popcll(__ballot(lanemax >= cand)) >= q) P = cand;
       }
-      if (lane == 0) s_red[wv] = P;
+      if (lane == 0) sm.red[wv] = P;
       __syncthreads();
-      uint32_t tau = s_red[0];
+      uint32_t tau = sm.red[0];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) tau = min(tau, s_red[w]);
+      for (int w = 1; w < kWaves; ++w) tau = min(tau, sm.red[w]);
+      const float tau_f = u2f(tau);
       // (2) gather the candidates (key >= tau) into LDS in index order
       uint32_t cnt[CPT], pos[CPT], C;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         uint32_t n = 0;
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const int i = c * kChunkSpan + tid * kChunk + e;
-          n += (i < L && (f2u(a[c][e]) & 0x7fffffffu) >= tau) ? 1u : 0u;
-        }
+        for (int e = 0; e < kChunk; ++e)
+          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) >= tau_f) ? 1u : 0u;
         cnt[c] = n;
       }
-      ordered_offsets<CPT>(cnt, pos, C, s_cnt);
+      ordered_offsets<CPT>(cnt, pos, C, sm.cnt);
       if (C <= (uint32_t)kCandMax) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-          if (cnt[c] == 0) continue;
           uint32_t p = pos[c];
 #pragma unroll
           for (int e = 0; e < kChunk; ++e) {
             const int i = c * kChunkSpan + tid * kChunk + e;
-            if (i < L && (f2u(a[c][e]) & 0x7fffffffu) >= tau) {
-              s_candA[p] = f2u(a[c][e]);
-              s_candI[p] = (uint16_t)i;
-              ++p;
-            }
+            // written as !(x < tau) so it is recomputed rather than kept
+            // from the counting pass (the same test for finite values)
+            const bool cd = MA_VALID(i) && !(fabsf(a[c][e]) < tau_f);
+            if (cd) sm.cand[p] = make_uint2(f2u(a[c][e]), (uint32_t)i);
+            p += cd ? 1u : 0u;
           }
         }
         __syncthreads();
-        // (3) one wave: exact k_b-th largest key by MSB-first bit search over
-        // the candidates, the tie cut in index order, and the ordered write
-        // of (I, bf16(V)) into the window row (ring_write).
+        // (3) one wave: the exact k_b-th largest key by MSB-first bit search,
+        // the tie cut in index order, and the ordered write of (I, bf16(V))
+        // into the window row (ring_write).
         if (wv == 0) {
           const int R = ((int)C + 63) >> 6;
           uint32_t ck[kCandMax / 64];
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r) {
-            const int cidx = r * 64 + lane;
-            ck[r] = (r < R && cidx < (int)C) ? (s_candA[cidx] & 0x7fffffffu) : 0u;
+            const int ci = r * 64 + lane;
+            ck[r] = (r < R && ci < (int)C) ? (sm.cand[ci].x & 0x7fffffffu) : 0u;
           }
-          // padding lanes hold key 0 but are excluded by the index test
           uint32_t Pk = 0;
           for (int b = 30; b >= 0; --b) {
             const uint32_t cand = Pk | (1u << b);
@@ -333,11 +383,14 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
               if (r < R) n += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] >= cand));
             if (n >= kb) Pk = cand;
           }
-          int ngt = 0;
+          int ngt = 0, ntie = 0;
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r)
-            if (r < R) ngt += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] > Pk));
-          const int need = kb - ngt;   // >= 1 ties at key Pk are taken
+            if (r < R) {
+              ngt += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] > Pk));
+              ntie += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] == Pk));
+            }
+          const int need = kb - ngt;   // >= 1 elements with key Pk are taken
           int run = 0, last = -1;
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r) {
@@ -347,41 +400,41 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
               const int pc = (int)__popcll(m);
               if (run + pc >= need) {
                 const bool hit = tie && (int)lanes_below(m) == need - run - 1;
-                const uint64_t hm = __ballot(hit);
-                const int src = __ffsll((long long)hm) - 1;
-                last = __shfl((int)s_candI[r * 64 + lane], src, 64);
+                const int src = __ffsll((long long)__ballot(hit)) - 1;
+                last = __shfl((int)sm.cand[r * 64 + lane].y, src, 64);
               }
               run += pc;
             }
           }
-          // ring_write: selected candidates, already in index order
           uint32_t *dst = A.G + A.row_base + off;
           int wrote = 0;
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r) {
             if (r < R) {
-              const int cidx = r * 64 + lane;
-              const bool in = cidx < (int)C;
-              const int idx = in ? (int)s_candI[cidx] : 0;
+              const int ci = r * 64 + lane;
+              const bool in = ci < (int)C;
+              const int idx = in ? (int)sm.cand[ci].y : 0;
               const bool sel = in && (ck[r] > Pk || (ck[r] == Pk && idx <= last));
               const uint64_t m = __ballot(sel);
-              if (sel) {
-                const float v = u2f(s_candA[cidx]);
-                dst[wrote + (int)lanes_below(m)] = (uint32_t)idx | (f32_to_bf16_rne(v) << 16);
-              }
+              if (sel) dst[wrote + (int)lanes_below(m)] = (uint32_t)idx | (f32_to_bf16_rne(u2f(sm.cand[ci].x)) << 16);
               wrote += (int)__popcll(m);
             }
           }
-          if (lane == 0) { s_sel[0] = Pk; s_sel[1] = (uint32_t)last; }
+          if (lane == 0) {
+            sm.sel[0] = Pk;
+            sm.sel[1] = (uint32_t)last;
+            sm.sel[2] = (ntie == need) ? 1u : 0u;
+          }
         }
         __syncthreads();
-        T = s_sel[0];
-        idx_last = (int)s_sel[1];
+        T = sm.sel[0];
+        idx_last = (int)sm.sel[1];
+        exact = sm.sel[2] != 0;
         done = true;
       }
     }
     if (!done) {
-      // General path (k_b > 8*64, k_b == L, or too many candidates): exact
+      // General path (k_b > 512, k_b == L, or too many candidates): exact
       // MSB-first bit search over the whole block with workgroup counts.
       uint32_t P = 0;
       for (int b = 30; b >= 0; --b) {
@@ -390,49 +443,43 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c)
 #pragma unroll
-          for (int e = 0; e < kChunk; ++e) {
-            const int i = c * kChunkSpan + tid * kChunk + e;
-            n += (i < L && (f2u(a[c][e]) & 0x7fffffffu) >= cand) ? 1u : 0u;
-          }
-        if ((int)block_sum(n, s_red) >= kb) P = cand;
+          for (int e = 0; e < kChunk; ++e)
+            n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) >= u2f(cand)) ? 1u : 0u;
+        if ((int)block_sum(n, sm.red) >= kb) P = cand;
       }
       uint32_t ngt = 0;
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const int i = c * kChunkSpan + tid * kChunk + e;
-          ngt += (i < L && (f2u(a[c][e]) & 0x7fffffffu) > P) ? 1u : 0u;
-        }
-      const int need = kb - (int)block_sum(ngt, s_red);
-      // the need-th tie (key == P) in index order
+        for (int e = 0; e < kChunk; ++e)
+          ngt += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) > u2f(P)) ? 1u : 0u;
+      const int need = kb - (int)block_sum(ngt, sm.red);
       uint32_t cnt[CPT], pos[CPT], tot;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         uint32_t n = 0;
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e) {
-          const int i = c * kChunkSpan + tid * kChunk + e;
-          n += (i < L && (f2u(a[c][e]) & 0x7fffffffu) == P) ? 1u : 0u;
-        }
+        for (int e = 0; e < kChunk; ++e)
+          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) == u2f(P)) ? 1u : 0u;
         cnt[c] = n;
       }
-      ordered_offsets<CPT>(cnt, pos, tot, s_cnt);
+      ordered_offsets<CPT>(cnt, pos, tot, sm.cnt);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         uint32_t p = pos[c];
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          if (i < L && (f2u(a[c][e]) & 0x7fffffffu) == P) {
-            if ((int)p == need - 1) s_sel[1] = (uint32_t)i;
+          if (MA_VALID(i) && fabsf(a[c][e]) == u2f(P)) {
+            if ((int)p == need - 1) sm.sel[1] = (uint32_t)i;
             ++p;
           }
         }
       }
       __syncthreads();
       T = P;
-      idx_last = (int)s_sel[1];
+      idx_last = (int)sm.sel[1];
+      exact = ((int)tot == need);
       // ring_write of every selected element, in index order
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -440,12 +487,12 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          const uint32_t key = f2u(a[c][e]) & 0x7fffffffu;
-          n += (i < L && (key > T || (key == T && i <= idx_last))) ? 1u : 0u;
+          const float x = fabsf(a[c][e]);
+          n += (MA_VALID(i) && (x > u2f(T) || (x == u2f(T) && i <= idx_last))) ? 1u : 0u;
         }
         cnt[c] = n;
       }
-      ordered_offsets<CPT>(cnt, pos, tot, s_cnt);
+      ordered_offsets<CPT>(cnt, pos, tot, sm.cnt);
       uint32_t *dst = A.G + A.row_base + off;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -453,8 +500,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          const uint32_t key = f2u(a[c][e]) & 0x7fffffffu;
-          if (i < L && (key > T || (key == T && i <= idx_last))) {
+          const float x = fabsf(a[c][e]);
+          if (MA_VALID(i) && (x > u2f(T) || (x == u2f(T) && i <= idx_last))) {
             dst[p] = (uint32_t)i | (f32_to_bf16_rne(a[c][e]) << 16);
             ++p;
           }
@@ -463,65 +510,79 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
     }
   }
 
-  if (!use_ef) return;   // no error feedback: codes and statistics are left as they are
+  if (!EF) return;   // no error feedback: codes and statistics are left as they are
 
   // ---------------- zero the selected entries; block min / max of the residual
   float mn = __int_as_float(0x7f800000), mx = -__int_as_float(0x7f800000);
+  if (exact) {
+    // every element with key T is selected: selected <=> |a| >= T
+    const float T_f = u2f(T);
 #pragma unroll
-  for (int c = 0; c < CPT; ++c)
+    for (int c = 0; c < CPT; ++c)
 #pragma unroll
-    for (int e = 0; e < kChunk; ++e) {
-      const int i = c * kChunkSpan + tid * kChunk + e;
-      const uint32_t key = f2u(a[c][e]) & 0x7fffffffu;
-      if (key > T || (key == T && i <= idx_last)) a[c][e] = 0.0f;
-      if (i < L) {
-        mn = fminf(mn, a[c][e]);
-        mx = fmaxf(mx, a[c][e]);
+      for (int e = 0; e < kChunk; ++e) {
+        const int i = c * kChunkSpan + tid * kChunk + e;
+        a[c][e] = (fabsf(a[c][e]) < T_f) ? a[c][e] : 0.0f;
+        if (MA_VALID(i)) {
+          mn = fminf(mn, a[c][e]);
+          mx = fmaxf(mx, a[c][e]);
+        }
       }
-    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        const int i = c * kChunkSpan + tid * kChunk + e;
+        const float x = fabsf(a[c][e]);
+        const bool sel = x > u2f(T) || (x == u2f(T) && i <= idx_last);
+        a[c][e] = sel ? 0.0f : a[c][e];
+        if (MA_VALID(i)) {
+          mn = fminf(mn, a[c][e]);
+          mx = fmaxf(mx, a[c][e]);
+        }
+      }
+  }
   mn = wave_min(mn);
   mx = wave_max(mx);
-  if (lane == 0) { s_redf[wv] = mn; s_redf[kWaves + wv] = mx; }
+  if (lane == 0) { sm.redf[wv] = mn; sm.redf[kWaves + wv] = mx; }   // uniform values
   __syncthreads();
-  mn = s_redf[0];
-  mx = s_redf[kWaves];
+  mn = sm.redf[0];
+  mx = sm.redf[kWaves];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) {
-    mn = fminf(mn, s_redf[w]);
-    mx = fmaxf(mx, s_redf[kWaves + w]);
+    mn = fminf(mn, sm.redf[w]);
+    mx = fmaxf(mx, sm.redf[kWaves + w]);
   }
   mn = mn + 0.0f;   // a zero extreme is stored as +0
   mx = mx + 0.0f;
 
-  // ---------------- ef_requant: unbiased stochastic 4-bit rounding
-  const bool flat = (mx == mn);
-  const float inv = flat ? 0.f : 15.0f / (mx - mn);
+  // ---------------- ef_requant: unbiased stochastic 4-bit rounding.  A
+  // constant block, or one whose scale 15/(Delta - delta) overflows fp32,
+  // gets code 0 everywhere.
+  const float inv = (mx == mn) ? 0.f : 15.0f / (mx - mn);
+  const bool flat = (mx == mn) || !(inv <= 3.402823466e38f);
   const uint32_t bkey = philox_block_key(A.seed, A.t, j);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int i0 = c * kChunkSpan + tid * kChunk;
     uint32_t packed = 0;
+    if (!flat) {
 #pragma unroll
-    for (int pr = 0; pr < kChunk / 2; ++pr) {
-      const uint32_t h = pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int e = 2 * pr + half;
-        const uint32_t u = half ? (h >> 16) : (h & 0xffffu);
-        uint32_t code = 0;
-        if (!flat) {
-          const float y = (a[c][e] - mn) * inv;
-          const float f = floorf(y);
-          const float frac = y - f;
-          code = (uint32_t)f + (((float)u < frac * 65536.0f) ? 1u : 0u);
-          code = min(code, 15u);
-        }
-        if (i0 + e >= L) code = 0;
-        packed |= code << (4 * e);
+      for (int pr = 0; pr < kChunk / 2; ++pr) {
+        const uint32_t nh = ~pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
+        const uint32_t c0 = quant_code(a[c][2 * pr], mn, inv, nh & 0xffffu);
+        const uint32_t c1 = quant_code(a[c][2 * pr + 1], mn, inv, nh >> 16);
+        packed |= (c0 << (8 * pr)) | (c1 << (8 * pr + 4));
       }
     }
+    if (!FULL) {
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e)
+        if (i0 + e >= L) packed &= ~(15u << (4 * e));
+    }
     if (ALIGNED) {
-      if (i0 < L) *reinterpret_cast<uint32_t *>(A.ef + ((s + i0) >> 1)) = packed;
+      if (FULL || i0 < L) *reinterpret_cast<uint32_t *>(A.ef + ((s + i0) >> 1)) = packed;
     } else {
       // neighbouring blocks (and threads) may share a code byte: change only
       // this element's nibble, by xor-ing old ^ new into its 32-bit word
@@ -544,6 +605,32 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A) {
     A.stats[2 * j] = mn;
     A.stats[2 * j + 1] = mx;
   }
+#undef MA_VALID
+}
+
+// The compressor kernels: one workgroup per block.  compress_full_kernel
+// serves blocks whose every element exists and is aligned (B_d = CPT * 4096,
+// 16-byte aligned gradients): blocks 0 .. grid-1.  compress_kernel serves the
+// rest with bounds tests: blocks first_block .. first_block + grid - 1.
+template <int CPT, bool EF>
+__global__ __launch_bounds__(kThreads, 4) void compress_full_kernel(CompressArgs A) {
+  __shared__ CompressSmem<CPT> sm;
+  const int64_t j = xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  const int64_t s = j * (int64_t)A.B;
+  const int64_t off = A.off_tab[j];
+  const int kb = (int)(A.off_tab[j + 1] - off);
+  compress_block<CPT, true, true, EF>(A, sm, j, s, CPT * kChunkSpan, off, kb);
+}
+
+template <int CPT, bool ALIGNED, bool EF>
+__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A, int64_t first_block) {
+  __shared__ CompressSmem<CPT> sm;
+  const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  const int64_t s = j * (int64_t)A.B;
+  const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
+  const int64_t off = A.off_tab[j];
+  const int kb = (int)(A.off_tab[j + 1] - off);
+  compress_block<CPT, false, ALIGNED, EF>(A, sm, j, s, L, off, kb);
 }
 
 // ------------------------------------------------------------------ adamstats_apply
@@ -558,15 +645,21 @@ struct ApplyArgs {
   unsigned long long *touched;   // optional: sum of touched positions
   int64_t d, k, n_b;
   int32_t B, m, tm, cap;    // tm = t mod m; cap = LDS slots per pass
+  int32_t ent_cap;          // window entries the LDS copy holds (m*k_b must fit to use it)
   float c1, c2, lr, eps, decay;
 };
 
 enum { kModeSparse = 0, kModeDense = 1, kModeMoments = 2 };
+constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
 
 // MODE 0: only touched parameters are read and written (decay must be 1).
 // MODE 1: the block's parameters are streamed through registers; decoupled
 //         decay on all, the Adam step on the touched ones.
 // MODE 2: write m_hat and v_hat of listed blocks; parameters untouched.
+//
+// LDS: bitmap of touched positions (W words), per-word slot base (W words),
+// the block's window entries (ent_cap words, when m*k_b fits), and per slot
+// z1, z2 (fp32) and its position (u16), cap slots per pass.
 template <int CPT, int MODE, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   extern __shared__ uint32_t smem[];
@@ -574,7 +667,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   constexpr int WPT = (W + kThreads - 1) / kThreads;
   uint32_t *s_bits = smem;
   uint32_t *s_wbase = smem + W;
-  float *s_z1 = reinterpret_cast<float *>(smem + 2 * W);
+  uint32_t *s_ent = smem + 2 * W;
+  float *s_z1 = reinterpret_cast<float *>(s_ent + A.ent_cap);
   float *s_z2 = s_z1 + A.cap;
   uint16_t *s_pos = reinterpret_cast<uint16_t *>(s_z2 + A.cap);
   __shared__ uint32_t s_cnt[kWaves + 1];
@@ -585,6 +679,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
   const int kb = (int)(A.off_tab[j + 1] - off);
+  const int M = A.m;
+  const bool in_lds = M * kb <= A.ent_cap;
 
   float th[CPT][kChunk];
   if (MODE == kModeDense) {
@@ -603,21 +699,32 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
     }
   }
 
-  // ---------------- union of the window's positions in this block
   for (int w = tid; w < W; w += kThreads) s_bits[w] = 0;
   __syncthreads();
-  for (int i = 0; i < A.m; ++i) {
-    const uint32_t *row = A.G + (int64_t)i * A.k + off;
+
+  // ---------------- the block's window entries: one pass over global memory
+  // (8 rows in flight per thread), copied to LDS when they fit; union bitmap.
+  // A zero value adds nothing (unwritten rows are all zero); an index outside
+  // the block (only possible in an imported state) is ignored.
+  for (int i0 = 0; i0 < M; i0 += 8) {
     for (int q = tid; q < kb; q += kThreads) {
-      const uint32_t e = row[q];
-      // a zero value adds nothing (unwritten rows are all zero); an index
-      // outside the block (only possible in an imported state) is ignored
-      if ((e & 0x7fff0000u) && (int)(e & 0xffffu) < L) atomicOr(&s_bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+      uint32_t e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        e[u] = (i0 + u < M) ? A.G[(int64_t)(i0 + u) * A.k + off + q] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u < M) {
+          if (in_lds) s_ent[(i0 + u) * kb + q] = e[u];
+          if ((e[u] & 0x7fff0000u) && (int)(e[u] & 0xffffu) < L)
+            atomicOr(&s_bits[(e[u] & 0xffffu) >> 5], 1u << (e[u] & 31u));
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---------------- compact slots: slot(p) = #touched positions below p
+  // ---------------- compact slots: slot(p) = number of touched positions below p
   uint32_t wc[WPT], mine = 0;
 #pragma unroll
   for (int r = 0; r < WPT; ++r) {
@@ -637,7 +744,6 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
     }
   }
   if (MODE != kModeMoments && A.touched && tid == 0) atomicAdd(A.touched, (unsigned long long)U);
-  __syncthreads();
 
   if (MODE == kModeDense) {
 #pragma unroll
@@ -657,9 +763,13 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
         }
       }
   }
+  // sparse update: slots per pass limited by what the threads hold in flight
+  const uint32_t pass = (MODE == kModeSparse) ? min((uint32_t)A.cap, (uint32_t)(kThreads * kThetaPerThread))
+                                              : (uint32_t)A.cap;
+  __syncthreads();
 
-  for (uint32_t s0 = 0; s0 < U; s0 += (uint32_t)A.cap) {
-    const uint32_t n = min((uint32_t)A.cap, U - s0);
+  for (uint32_t s0 = 0; s0 < U; s0 += pass) {
+    const uint32_t n = min(pass, U - s0);
     for (uint32_t x = (uint32_t)tid; x < n; x += kThreads) { s_z1[x] = 0.f; s_z2[x] = 0.f; }
     if (MODE == kModeSparse) {
 #pragma unroll
@@ -678,14 +788,23 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
       }
     }
     __syncthreads();
+    // the touched parameters of this pass, loaded before the row scatter so
+    // their latency overlaps it
+    float thv[kThetaPerThread];
+    if (MODE == kModeSparse) {
+#pragma unroll
+      for (int u = 0; u < kThetaPerThread; ++u) {
+        const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+        thv[u] = (x < n) ? A.theta[s + s_pos[x]] : 0.f;
+      }
+    }
     // AdamStats: z[I] += beta^r V, rows in physical order, one row at a time
-    for (int i = 0; i < A.m; ++i) {
+    for (int i = 0; i < M; ++i) {
       int r = A.tm - i;
-      if (r < 0) r += A.m;
-      const float f1 = A.betapow[r], f2 = A.betapow[A.m + r];
-      const uint32_t *row = A.G + (int64_t)i * A.k + off;
+      if (r < 0) r += M;
+      const float f1 = A.betapow[r], f2 = A.betapow[M + r];
       for (int q = tid; q < kb; q += kThreads) {
-        const uint32_t e = row[q];
+        const uint32_t e = in_lds ? s_ent[i * kb + q] : A.G[(int64_t)i * A.k + off + q];
         const uint32_t I = e & 0xffffu;
         if (!(e & 0x7fff0000u) || (int)I >= L) continue;
         const float V = bf16_bits_to_f32(e >> 16);
@@ -699,13 +818,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
     }
     // m_hat = c1 z1, v_hat = c2 z2; theta -= lr * m_hat / (sqrt(v_hat) + eps)
     if (MODE == kModeSparse) {
-      for (uint32_t x = (uint32_t)tid; x < n; x += kThreads) {
-        const int p = s_pos[x];
-        const float mh = A.c1 * s_z1[x];
-        const float vh = A.c2 * s_z2[x];
-        float *tp = A.theta + s + p;
-        const float upd = A.lr * (mh / (sqrtf(vh) + A.eps));
-        *tp = *tp - upd;
+#pragma unroll
+      for (int u = 0; u < kThetaPerThread; ++u) {
+        const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+        if (x < n) {
+          const float mh = A.c1 * s_z1[x];
+          const float vh = A.c2 * s_z2[x];
+          A.theta[s + s_pos[x]] = thv[u] - A.lr * (mh / (sqrtf(vh) + A.eps));
+        }
       }
     } else {
 #pragma unroll

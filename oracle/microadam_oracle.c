@@ -18,6 +18,7 @@
  */
 #include "microadam_oracle.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -239,11 +240,13 @@ void orc_group_minmax(const float *x, int64_t n, float *lo, float *hi)
 void orc_quant_group(const float *x, int64_t n, uint64_t seed, int64_t t, int64_t j,
                      int64_t local0, float lo, float hi, uint8_t *codes_out)
 {
-    if (hi == lo) {
+    /* Reading: when 15/(Delta - delta) has no finite fp32 value (a range below
+     * about 4.4e-38) the group is treated like a constant one. */
+    float inv = (hi == lo) ? 0.0f : 15.0f / (hi - lo);
+    if (hi == lo || !(inv <= FLT_MAX)) {
         for (int64_t i = 0; i < n; ++i) codes_out[i] = 0;
         return;
     }
-    float inv = 15.0f / (hi - lo);
     for (int64_t i = 0; i < n; ++i) {
         float y = (x[i] - lo) * inv;
         float f = floorf(y);
