@@ -58,7 +58,9 @@ enum {
 
 /* Flags for ma_set_flags. */
 #define MA_FLAG_NO_EF 1u        /* a_t = g_t: stored error neither read nor rewritten */
-#define MA_FLAG_FORCE_DENSE 4u  /* stream all of theta in the update (same results) */
+#define MA_FLAG_FORCE_DENSE 4u  /* stream the parameters in the update (same results) */
+#define MA_FLAG_FORCE_SPARSE 8u /* gather only touched parameters (same results; ignored
+                                   when weight decay makes every parameter change) */
 
 /* State buffers for ma_read_state / ma_write_state. */
 #define MA_STATE_CODES 0
@@ -93,8 +95,10 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
 size_t ma_state_bytes(const ma_ctx *h);
 
 /* Everything else the library holds on the device: per-block statistics
- * (8*n_b), the block offset table (8*(n_b+1)), the beta-power table (8*m) and
- * the code buffer's tail padding.  0 for NULL. */
+ * (8*n_b), the block offset table (8*(n_b+1)), the beta-power table (8*m),
+ * the code buffer's tail padding, the touched-parameter counters (8 KiB) and the
+ * compressor's deferred-block list (8*n_b + 256).
+ * 0 for NULL. */
 size_t ma_aux_bytes(const ma_ctx *h);
 
 /* Frees every device buffer of the handle; NULL is accepted. */
@@ -145,6 +149,19 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
  */
 int ma_set_timing(ma_ctx *h, int on);
 int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk);
+
+/*
+ * Overlap inside one step.  The blocks are cut into `chunks` contiguous ranges
+ * (1 <= chunks <= 64, at most n_b are used); the update of range i runs on a
+ * stream the handle owns (default priority), after the compressor of range i
+ * and concurrently with the compressor of range i+1, which stays on the
+ * caller's stream.  Ranges share no state, so results do not depend on
+ * `chunks`.  The caller's stream waits for the handle's stream before ma_step
+ * returns, so the step remains ordered on `stream` as one unit.  Default: 8
+ * when n_b >= 8192, else 1.  With timing on, the per-kernel times then include
+ * the time the two kernels spend sharing the device.
+ */
+int ma_set_pipeline(ma_ctx *h, int chunks);
 
 /* Counting of touched parameters (positions present in the window, i.e. the
  * parameters an update reads and writes), summed over blocks and steps.

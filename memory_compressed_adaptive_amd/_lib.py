@@ -20,6 +20,7 @@ MA_EHIP = -4
 
 MA_FLAG_NO_EF = 1
 MA_FLAG_FORCE_DENSE = 4
+MA_FLAG_FORCE_SPARSE = 8
 
 MA_STATE_CODES = 0
 MA_STATE_STATS = 1
@@ -30,7 +31,7 @@ EXPORTS = (
     "ma_create", "ma_step", "ma_state_bytes", "ma_aux_bytes", "ma_destroy", "ma_last_error",
     "ma_last_error_message", "ma_get_step", "ma_num_blocks", "ma_set_step", "ma_set_flags",
     "ma_set_lr", "ma_read_state", "ma_write_state", "ma_debug_moments", "ma_set_timing",
-    "ma_kernel_times", "ma_set_count_touched", "ma_touched_count",
+    "ma_kernel_times", "ma_set_pipeline", "ma_set_count_touched", "ma_touched_count",
 )
 
 _lib = None
@@ -85,6 +86,8 @@ def lib():
     L.ma_set_timing.argtypes = [p, C.c_int]
     L.ma_kernel_times.restype = C.c_int
     L.ma_kernel_times.argtypes = [p, p, p, C.c_int]
+    L.ma_set_pipeline.restype = C.c_int
+    L.ma_set_pipeline.argtypes = [p, C.c_int]
     L.ma_set_count_touched.restype = C.c_int
     L.ma_set_count_touched.argtypes = [p, C.c_int]
     L.ma_touched_count.restype = i64

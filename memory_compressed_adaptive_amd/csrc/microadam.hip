@@ -50,6 +50,7 @@ struct ma_ctx {
   int cpt = 1;       // 4096-element chunks per thread
   int cap = 0;       // LDS slots per pass of the update kernel
   int ent_cap = 0;   // window entries of one block the update kernel keeps in LDS
+  bool dense_default = false;   // stream the parameters in the update even without decay
   size_t apply_lds = 0;
 
   uint8_t *codes = nullptr;
@@ -60,14 +61,22 @@ struct ma_ctx {
   float *betapow = nullptr;
   unsigned long long *touched = nullptr;
   bool count_touched = false;
+  int64_t *deferred = nullptr;        // blocks handed from the full-block to the general compressor
+  unsigned int *n_deferred = nullptr;
 
   // last step's constants (for ma_debug_moments)
   float last_c1 = 0, last_c2 = 0;
 
+  // overlap of compress and update across block ranges (see ma_step)
+  int chunks = 1;
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+  std::vector<hipEvent_t> chunk_ev;
+
   bool timing = false;
-  struct Ev { hipEvent_t e[3]; };
-  std::vector<Ev> events;   // recorded, not yet read
-  std::vector<Ev> pool;     // free
+  struct Ev { int kernel; hipEvent_t start, end; };
+  std::vector<Ev> events;          // recorded, not yet read
+  std::vector<hipEvent_t> pool;    // free timing events
   double acc_ms[2] = {0, 0};
   int64_t acc_n[2] = {0, 0};
 };
@@ -82,12 +91,46 @@ void free_all(ma_ctx *h) {
   hipFree(h->off_tab);
   hipFree(h->betapow);
   hipFree(h->touched);
-  for (auto &ev : h->events)
-    for (auto e : ev.e) hipEventDestroy(e);
-  for (auto &ev : h->pool)
-    for (auto e : ev.e) hipEventDestroy(e);
+  hipFree(h->deferred);
+  hipFree(h->n_deferred);
+  for (auto &ev : h->events) {
+    hipEventDestroy(ev.start);
+    hipEventDestroy(ev.end);
+  }
+  for (auto e : h->pool) hipEventDestroy(e);
   h->events.clear();
   h->pool.clear();
+  for (auto e : h->chunk_ev) hipEventDestroy(e);
+  h->chunk_ev.clear();
+  if (h->fork_ev) hipEventDestroy(h->fork_ev);
+  if (h->join_ev) hipEventDestroy(h->join_ev);
+  if (h->side) hipStreamDestroy(h->side);
+  h->fork_ev = h->join_ev = nullptr;
+  h->side = nullptr;
+}
+
+// The side stream (default priority) and the events that order it against
+// the caller's stream, for `chunks` block ranges.
+bool ensure_pipeline(ma_ctx *h, int chunks) {
+  if (!h->side && hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) return false;
+  if (!h->fork_ev && hipEventCreateWithFlags(&h->fork_ev, hipEventDisableTiming) != hipSuccess) return false;
+  if (!h->join_ev && hipEventCreateWithFlags(&h->join_ev, hipEventDisableTiming) != hipSuccess) return false;
+  while ((int)h->chunk_ev.size() < chunks) {
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return false;
+    h->chunk_ev.push_back(ev);
+  }
+  return true;
+}
+
+hipEvent_t timing_event(ma_ctx *h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  return hipEventCreate(&e) == hipSuccess ? e : nullptr;
 }
 
 int64_t floor_mul_div(int64_t k, int64_t x, int64_t d) {
@@ -109,35 +152,42 @@ struct DeviceGuard {
   }
 };
 
+// Compressor launches for blocks [b0, b1): blocks below n_full take the
+// bounds-free kernel (plus the kernel finishing what it deferred), the rest
+// the general one.  a.deferred / a.n_deferred are this range's list.
 template <int CPT, bool AL, bool EF>
-hipError_t launch_compress(const CompressArgs &a, int64_t n_full, int64_t n_b, hipStream_t s) {
-  if (CPT <= 4 && AL && n_full > 0)
-    hipLaunchKernelGGL((compress_full_kernel<(CPT <= 4 ? CPT : 4), EF>), dim3((unsigned)n_full), dim3(kThreads), 0,
-                       s, a);
-  if (n_b > n_full)
-    hipLaunchKernelGGL((compress_kernel<CPT, AL, EF>), dim3((unsigned)(n_b - n_full)), dim3(kThreads), 0, s, a,
-                       n_full);
+hipError_t launch_compress(const CompressArgs &a, int64_t b0, int64_t b1, int64_t n_full, hipStream_t s) {
+  const int64_t f1 = std::min(b1, n_full);
+  if (CPT <= 4 && AL && f1 > b0) {
+    constexpr int C4 = CPT <= 4 ? CPT : 4;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, a.n_deferred, 1);
+    hipLaunchKernelGGL((compress_full_kernel<C4, EF>), dim3((unsigned)(f1 - b0)), dim3(kThreads), 0, s, a, b0);
+    hipLaunchKernelGGL((compress_deferred_kernel<C4, EF>), dim3((unsigned)std::min<int64_t>(f1 - b0, 256)),
+                       dim3(kThreads), 0, s, a);
+  }
+  const int64_t g0 = std::max(b0, (CPT <= 4 && AL) ? n_full : (int64_t)0);
+  if (b1 > g0)
+    hipLaunchKernelGGL((compress_kernel<CPT, AL, EF>), dim3((unsigned)(b1 - g0)), dim3(kThreads), 0, s, a, g0);
   return hipGetLastError();
 }
 
 template <int CPT>
-hipError_t launch_compress_cpt(bool aligned, bool ef, const CompressArgs &a, int64_t n_full, int64_t n_b,
-                               hipStream_t s) {
+hipError_t launch_compress_cpt(bool aligned, bool ef, const CompressArgs &a, int64_t b0, int64_t b1,
+                               int64_t n_full, hipStream_t s) {
   if (ef)
-    return aligned ? launch_compress<CPT, true, true>(a, n_full, n_b, s)
-                   : launch_compress<CPT, false, true>(a, n_full, n_b, s);
-  return aligned ? launch_compress<CPT, true, false>(a, n_full, n_b, s)
-                 : launch_compress<CPT, false, false>(a, n_full, n_b, s);
+    return aligned ? launch_compress<CPT, true, true>(a, b0, b1, n_full, s)
+                   : launch_compress<CPT, false, true>(a, b0, b1, n_full, s);
+  return aligned ? launch_compress<CPT, true, false>(a, b0, b1, n_full, s)
+                 : launch_compress<CPT, false, false>(a, b0, b1, n_full, s);
 }
 
-// Blocks 0 .. n_full-1 take the bounds-free kernel; the rest the general one.
-hipError_t dispatch_compress(int cpt, bool aligned, bool ef, const CompressArgs &a, int64_t n_full, int64_t n_b,
-                             hipStream_t s) {
+hipError_t dispatch_compress(int cpt, bool aligned, bool ef, const CompressArgs &a, int64_t b0, int64_t b1,
+                             int64_t n_full, hipStream_t s) {
   switch (cpt) {
-    case 1: return launch_compress_cpt<1>(aligned, ef, a, n_full, n_b, s);
-    case 2: return launch_compress_cpt<2>(aligned, ef, a, n_full, n_b, s);
-    case 4: return launch_compress_cpt<4>(aligned, ef, a, n_full, n_b, s);
-    default: return launch_compress_cpt<8>(aligned, ef, a, 0, n_b, s);
+    case 1: return launch_compress_cpt<1>(aligned, ef, a, b0, b1, n_full, s);
+    case 2: return launch_compress_cpt<2>(aligned, ef, a, b0, b1, n_full, s);
+    case 4: return launch_compress_cpt<4>(aligned, ef, a, b0, b1, n_full, s);
+    default: return launch_compress_cpt<8>(aligned, ef, a, b0, b1, 0, s);
   }
 }
 
@@ -244,6 +294,9 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
   const int64_t cap_limit = ((int64_t)kApplyLdsLimit - 8 * (int64_t)W - 4 * (int64_t)h->ent_cap) / 10;
   h->cap = (int)std::max<int64_t>(1, std::min<int64_t>(umax, cap_limit));
   h->apply_lds = 8 * (size_t)W + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
+  // expected fraction of positions present in a full window: 1 - (1 - k/d)^m
+  h->dense_default = false;   // measured: gathering touched parameters wins at m = 1 and m = 10
+  h->chunks = h->n_b >= 8192 ? 8 : 1;
 
   h->codes_bytes = (size_t)((d + 1) / 2);
   h->codes_alloc = (h->codes_bytes + 15) & ~(size_t)15;
@@ -254,7 +307,9 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
             hipMalloc(&h->window, win_b ? win_b : 4) == hipSuccess &&
             hipMalloc(&h->off_tab, 8 * off.size()) == hipSuccess &&
             hipMalloc(&h->betapow, 4 * bp.size()) == hipSuccess &&
-            hipMalloc(&h->touched, sizeof(unsigned long long)) == hipSuccess;
+            hipMalloc(&h->touched, kTouchedSlots * sizeof(unsigned long long)) == hipSuccess &&
+            hipMalloc(&h->deferred, 8 * (size_t)h->n_b) == hipSuccess &&
+            hipMalloc(&h->n_deferred, 64 * sizeof(unsigned int)) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     free_all(h);
@@ -268,7 +323,7 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
        hipMemset(h->window, 0, win_b ? win_b : 4) == hipSuccess &&
        hipMemcpy(h->off_tab, off.data(), 8 * off.size(), hipMemcpyHostToDevice) == hipSuccess &&
        hipMemcpy(h->betapow, bp.data(), 4 * bp.size(), hipMemcpyHostToDevice) == hipSuccess &&
-       hipMemset(h->touched, 0, sizeof(unsigned long long)) == hipSuccess &&
+       hipMemset(h->touched, 0, kTouchedSlots * sizeof(unsigned long long)) == hipSuccess &&
        hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     const hipError_t e = hipGetLastError();
@@ -295,7 +350,8 @@ size_t ma_state_bytes(const ma_ctx *h) {
 size_t ma_aux_bytes(const ma_ctx *h) {
   if (!h) return 0;
   return 8 * (size_t)h->n_b + 8 * ((size_t)h->n_b + 1) + 8 * (size_t)h->m +
-         (h->codes_alloc - h->codes_bytes) + sizeof(unsigned long long);
+         (h->codes_alloc - h->codes_bytes) + kTouchedSlots * sizeof(unsigned long long) +
+         8 * (size_t)h->n_b + 64 * sizeof(unsigned int);
 }
 
 int64_t ma_get_step(const ma_ctx *h) { return h ? h->t : -1; }
@@ -311,7 +367,8 @@ int ma_set_step(ma_ctx *h, int64_t t) {
 int ma_set_flags(ma_ctx *h, uint32_t flags) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_flags: null handle");
-  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE)) return fail(MA_EINVAL, "ma_set_flags: unknown flag bits");
+  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE))
+    return fail(MA_EINVAL, "ma_set_flags: unknown flag bits");
   h->flags = flags;
   return MA_OK;
 }
@@ -351,6 +408,8 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   ca.row_base = (t % h->m) * h->k;
   ca.seed = h->seed;
   ca.B = h->B;
+  ca.deferred = h->deferred;
+  ca.n_deferred = h->n_deferred;
 
   ApplyArgs aa = make_apply_args(h, t, c1, c2, decay);
   aa.theta = params;
@@ -359,26 +418,66 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   const bool b8 = (h->B % 8) == 0;
   const bool g_al = b8 && (((uintptr_t)grads & 15u) == 0);
   const bool p_al = b8 && (((uintptr_t)params & 15u) == 0);
-  const int mode = (decay != 1.0f || (h->flags & MA_FLAG_FORCE_DENSE)) ? kModeDense : kModeSparse;
+  // Update mode: decoupled decay touches every parameter (dense); otherwise
+  // only the touched parameters are gathered by slot (sparse), which measured
+  // faster than streaming at both m = 1 and m = 10 on the LLaMA-2-7B shape.
+  int mode = h->dense_default ? kModeDense : kModeSparse;
+  if (h->flags & MA_FLAG_FORCE_DENSE) mode = kModeDense;
+  if (h->flags & MA_FLAG_FORCE_SPARSE) mode = kModeSparse;
+  if (decay != 1.0f) mode = kModeDense;
 
-  ma_ctx::Ev ev{};
-  if (h->timing) {
-    if (!h->pool.empty()) {
-      ev = h->pool.back();
-      h->pool.pop_back();
-    } else {
-      for (auto &e : ev.e)
-        if (hipEventCreate(&e) != hipSuccess) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
-    }
-    hipEventRecord(ev.e[0], stream);
-  }
+  // The blocks are cut into h->chunks ranges.  Compress of range i runs on
+  // the caller's stream; the update of range i runs on the library's side
+  // stream once compress i is done, so it overlaps compress i+1 (one kernel
+  // is bound by arithmetic, the other by memory).  The caller's stream waits
+  // for the side stream at the end: ma_step stays one asynchronous step on
+  // `stream`.
   const int64_t n_full = (g_al && h->B == h->cpt * kChunkSpan) ? h->d / h->B : 0;
-  hipError_t e = dispatch_compress(h->cpt, g_al, !(h->flags & MA_FLAG_NO_EF), ca, n_full, h->n_b, stream);
-  if (e == hipSuccess && h->timing) hipEventRecord(ev.e[1], stream);
-  if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream);
-  if (h->timing) {
-    hipEventRecord(ev.e[2], stream);
-    h->events.push_back(ev);
+  const bool ef = !(h->flags & MA_FLAG_NO_EF);
+  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
+  hipError_t e = hipSuccess;
+  if (chunks > 1 && !ensure_pipeline(h, chunks)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
+  hipStream_t upd = chunks > 1 ? h->side : stream;
+  if (chunks > 1) {
+    e = hipEventRecord(h->fork_ev, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
+  }
+  for (int i = 0; i < chunks && e == hipSuccess; ++i) {
+    const int64_t b0 = h->n_b * i / chunks, b1 = h->n_b * (i + 1) / chunks;
+    CompressArgs cai = ca;
+    cai.deferred = h->deferred + b0;
+    cai.n_deferred = h->n_deferred + i;
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (h->timing && !(t0 = timing_event(h)) ) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (h->timing && !(t1 = timing_event(h)) ) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (t0) (void)hipEventRecord(t0, stream);
+    e = dispatch_compress(h->cpt, g_al, ef, cai, b0, b1, n_full, stream);
+    if (t1) {
+      (void)hipEventRecord(t1, stream);
+      h->events.push_back({0, t0, t1});
+    }
+    if (e != hipSuccess) break;
+    if (chunks > 1) {
+      e = hipEventRecord(h->chunk_ev[i], stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->chunk_ev[i], 0);
+      if (e != hipSuccess) break;
+    }
+    ApplyArgs aai = aa;
+    aai.first_block = b0;
+    hipEvent_t u0 = nullptr, u1 = nullptr;
+    if (h->timing && !(u0 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (h->timing && !(u1 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (u0) (void)hipEventRecord(u0, upd);
+    e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, h->apply_lds, upd);
+    if (u1) {
+      (void)hipEventRecord(u1, upd);
+      h->events.push_back({1, u0, u1});
+    }
+  }
+  if (chunks > 1) {
+    hipError_t e2 = hipEventRecord(h->join_ev, h->side);
+    if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, h->join_ev, 0);
+    if (e == hipSuccess) e = e2;
   }
   if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
   h->t = t;
@@ -458,7 +557,11 @@ int ma_set_timing(ma_ctx *h, int on) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_timing: null handle");
   DeviceGuard guard(h->device);
-  for (auto &ev : h->events) h->pool.push_back(ev);
+  if (hipDeviceSynchronize() != hipSuccess) return fail(MA_EHIP, "ma_set_timing: device synchronize failed");
+  for (auto &ev : h->events) {
+    h->pool.push_back(ev.start);
+    h->pool.push_back(ev.end);
+  }
   h->events.clear();
   h->acc_ms[0] = h->acc_ms[1] = 0;
   h->acc_n[0] = h->acc_n[1] = 0;
@@ -471,16 +574,13 @@ int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk) {
   if (!h || !ms_out || !launches_out || nk < 0 || nk > 2) return fail(MA_EINVAL, "ma_kernel_times: bad argument");
   DeviceGuard guard(h->device);
   for (auto &ev : h->events) {
-    if (hipEventSynchronize(ev.e[2]) != hipSuccess) return fail(MA_EHIP, "ma_kernel_times: event wait failed");
-    float a = 0, b = 0;
-    if (hipEventElapsedTime(&a, ev.e[0], ev.e[1]) != hipSuccess ||
-        hipEventElapsedTime(&b, ev.e[1], ev.e[2]) != hipSuccess)
-      return fail(MA_EHIP, "ma_kernel_times: elapsed time failed");
-    h->acc_ms[0] += a;
-    h->acc_ms[1] += b;
-    h->acc_n[0] += 1;
-    h->acc_n[1] += 1;
-    h->pool.push_back(ev);
+    float ms = 0;
+    if (hipEventSynchronize(ev.end) != hipSuccess || hipEventElapsedTime(&ms, ev.start, ev.end) != hipSuccess)
+      return fail(MA_EHIP, "ma_kernel_times: reading an event failed");
+    h->acc_ms[ev.kernel] += ms;
+    h->acc_n[ev.kernel] += 1;
+    h->pool.push_back(ev.start);
+    h->pool.push_back(ev.end);
   }
   h->events.clear();
   for (int i = 0; i < nk; ++i) {
@@ -490,12 +590,19 @@ int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk) {
   return MA_OK;
 }
 
+int ma_set_pipeline(ma_ctx *h, int chunks) {
+  clear_error();
+  if (!h || chunks < 1 || chunks > 64) return fail(MA_EINVAL, "ma_set_pipeline: chunks must be in [1, 64]");
+  h->chunks = chunks;
+  return MA_OK;
+}
+
 int ma_set_count_touched(ma_ctx *h, int on) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_count_touched: null handle");
   DeviceGuard guard(h->device);
   if (on && (hipDeviceSynchronize() != hipSuccess ||
-             hipMemset(h->touched, 0, sizeof(unsigned long long)) != hipSuccess ||
+             hipMemset(h->touched, 0, kTouchedSlots * sizeof(unsigned long long)) != hipSuccess ||
              hipDeviceSynchronize() != hipSuccess))
     return fail(MA_EHIP, "ma_set_count_touched: clearing the counter failed");
   h->count_touched = on != 0;
@@ -506,13 +613,15 @@ int64_t ma_touched_count(ma_ctx *h) {
   clear_error();
   if (!h || !h->count_touched) return -1;
   DeviceGuard guard(h->device);
-  unsigned long long v = 0;
+  std::vector<unsigned long long> v(kTouchedSlots);
   if (hipDeviceSynchronize() != hipSuccess ||
-      hipMemcpy(&v, h->touched, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) {
+      hipMemcpy(v.data(), h->touched, kTouchedSlots * sizeof(unsigned long long), hipMemcpyDeviceToHost) != hipSuccess) {
     fail(MA_EHIP, "ma_touched_count: copy failed");
     return -1;
   }
-  return (int64_t)v;
+  unsigned long long sum = 0;
+  for (auto x : v) sum += x;
+  return (int64_t)sum;
 }
 
 }  // extern "C"

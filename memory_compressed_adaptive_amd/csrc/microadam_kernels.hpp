@@ -203,6 +203,8 @@ struct CompressArgs {
   int64_t row_base;         // (t mod m) * k
   uint64_t seed;
   int32_t B;
+  int64_t *deferred;        // blocks the full-block kernel hands to the general path
+  unsigned int *n_deferred; // their count
 };
 
 template <int CPT>
@@ -232,34 +234,90 @@ __device__ __forceinline__ uint32_t quant_code(float v, float lo, float inv, uin
 // loads), on 16-byte alignment of the gradient / 8-element alignment of the
 // block (ALIGNED: one 16-byte gradient load and one 4-byte code word per
 // thread and chunk) and on error feedback being on (EF).
-template <int CPT, bool FULL, bool ALIGNED, bool EF>
+// Inputs of one full block, staged ahead of its processing: the gradients and
+// the packed codes go straight from global memory into LDS (LDS-DMA loads,
+// no registers held while in flight), the block statistics and the window
+// offsets into registers.
+template <int CPT>
+struct FullBlockStage {
+  u32x4 g[CPT][kThreads];     // thread t's 8 gradients of chunk c at [c][t]
+  uint32_t ef[CPT][kThreads]; // thread t's 8 codes of chunk c at [c][t]
+};
+
+template <int CPT>
+struct FullBlockInputs {
+  float lo, hi;
+  int64_t off;
+  int kb;
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int CPT, bool EF>
+__device__ __forceinline__ void stage_full_block(const CompressArgs &A, int64_t j, FullBlockStage<CPT> &st,
+                                                 FullBlockInputs<CPT> &in) {
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wbase = tid & ~63;   // a wave's lanes fill 64 consecutive LDS slots
+  const int64_t s = j * (int64_t)A.B;
+  // uniform block bases plus 32-bit lane offsets (scalar-base addressing)
+  const u32x4 *gb = reinterpret_cast<const u32x4 *>(A.g + s);
+  const uint32_t *eb = reinterpret_cast<const uint32_t *>(A.ef + (s >> 1));
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gb + (c * kThreads + tid)),
+                                     (lds_void_t *)(&st.g[c][wbase]), 16, 0, 0);
+    if (EF)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(eb + (c * kThreads + tid)),
+                                       (lds_void_t *)(&st.ef[c][wbase]), 4, 0, 0);
+  }
+  in.lo = EF ? A.stats[2 * j] : 0.f;
+  in.hi = EF ? A.stats[2 * j + 1] : 0.f;
+  in.off = A.off_tab[j];
+  in.kb = (int)(A.off_tab[j + 1] - in.off);
+}
+
+// Waits until this wave's outstanding vector-memory operations (including its
+// LDS-DMA loads) are complete; the empty asm statements keep the compiler from
+// moving LDS reads across the wait.
+__device__ __forceinline__ void wait_vm_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), expcnt and lgkmcnt not waited on
+  asm volatile("" ::: "memory");
+}
+
+// FULL path: st / raw hold the block's staged inputs.
+// DEFER: a block the candidate path cannot finish (too many candidates, e.g.
+// massive ties) is appended to A.deferred untouched, for the general path.
+template <int CPT, bool FULL, bool ALIGNED, bool EF, bool DEFER = false>
 __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
-                                               int64_t s, int L, int64_t off, int kb) {
-  const int tid = (int)threadIdx.x, lane = lane_id(), wv = tid >> 6;
+                                               int64_t s, int L, int64_t off, int kb,
+                                               FullBlockStage<CPT> *st, const FullBlockInputs<CPT> *raw) {
+  // The thread index is passed through an empty asm statement so that, inside
+  // the persistent loop, values derived from it are recomputed per block
+  // instead of being hoisted out of the loop and held in (spilled) registers.
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wv = tid >> 6;
 
   // ---------------- ef_dequant_accumulate: a = f32(g) + fmaf(code, step, delta)
   float lo = 0.f, step = 0.f;
   if (EF) {
-    lo = A.stats[2 * j];
-    const float hi = A.stats[2 * j + 1];
+    lo = (FULL && ALIGNED) ? raw->lo : A.stats[2 * j];
+    const float hi = (FULL && ALIGNED) ? raw->hi : A.stats[2 * j + 1];
     step = (hi - lo) / 15.0f;
   }
   float a[CPT][kChunk];
   uint32_t oldc[CPT];
   if (FULL && ALIGNED) {
-    u32x4 gv[CPT];
-    uint32_t cw[CPT];
+    wait_vm_all();
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int i0 = c * kChunkSpan + tid * kChunk;
-      gv[c] = load_stream16(A.g + s + i0);
-      cw[c] = EF ? *reinterpret_cast<const uint32_t *>(A.ef + ((s + i0) >> 1)) : 0u;
-    }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      oldc[c] = cw[c];
-      const uint32_t gw[4] = {gv[c].x, gv[c].y, gv[c].z, gv[c].w};
-      const uint32_t ce = cw[c] & 0x0f0f0f0fu, co = (cw[c] >> 4) & 0x0f0f0f0fu;
+      const uint32_t cwc = EF ? st->ef[c][tid] : 0u;
+      const u32x4 gvc = st->g[c][tid];
+      oldc[c] = cwc;
+      const uint32_t gw[4] = {gvc.x, gvc.y, gvc.z, gvc.w};
+      const uint32_t ce = cwc & 0x0f0f0f0fu, co = (cwc >> 4) & 0x0f0f0f0fu;
 #pragma unroll
       for (int e = 0; e < kChunk; ++e) {
         const float gf = (e & 1) ? u2f(gw[e >> 1] & 0xffff0000u) : u2f(gw[e >> 1] << 16);
@@ -369,43 +427,73 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
         if (wv == 0) {
           const int R = ((int)C + 63) >> 6;
           uint32_t ck[kCandMax / 64];
+          uint32_t kmax = 0;
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r) {
             const int ci = r * 64 + lane;
             ck[r] = (r < R && ci < (int)C) ? (sm.cand[ci].x & 0x7fffffffu) : 0u;
+            kmax = max(kmax, ck[r]);
           }
-          uint32_t Pk = 0;
-          for (int b = 30; b >= 0; --b) {
+          kmax = f2u(wave_max(u2f(kmax)));   // non-negative floats order like their bits
+          // T lies in [tau, kmax], so it shares their common leading bits;
+          // search the rest MSB first.  Invariant: count(key >= Pk) >= k_b.
+          // Padding lanes hold key 0 and never reach a candidate value >= 1.
+          const uint32_t diff = tau ^ kmax;
+          const int hb = diff ? 31 - __clz(diff) : -1;
+          uint32_t Pk = diff ? (tau & ~((2u << hb) - 1u)) : tau;
+          bool cut = (diff == 0);   // all candidates share one key: T = tau, every tie taken
+          for (int b = hb; b >= 0 && !cut; --b) {
             const uint32_t cand = Pk | (1u << b);
             int n = 0;
 #pragma unroll
             for (int r = 0; r < kCandMax / 64; ++r)
-              if (r < R) n += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] >= cand));
-            if (n >= kb) Pk = cand;
-          }
-          int ngt = 0, ntie = 0;
+              if (r < R) n += (int)__popcll(__ballot(ck[r] >= cand));
+            if (n >= kb) {
+              Pk = cand;
+              if (n == kb) {
+                // exactly k_b keys reach cand: they are the selection and T is
+                // their smallest key (no key equal to it is left out)
+                uint32_t mn = 0xffffffffu;
 #pragma unroll
-          for (int r = 0; r < kCandMax / 64; ++r)
-            if (r < R) {
-              ngt += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] > Pk));
-              ntie += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] == Pk));
-            }
-          const int need = kb - ngt;   // >= 1 elements with key Pk are taken
-          int run = 0, last = -1;
-#pragma unroll
-          for (int r = 0; r < kCandMax / 64; ++r) {
-            if (r < R && last < 0) {
-              const bool tie = r * 64 + lane < (int)C && ck[r] == Pk;
-              const uint64_t m = __ballot(tie);
-              const int pc = (int)__popcll(m);
-              if (run + pc >= need) {
-                const bool hit = tie && (int)lanes_below(m) == need - run - 1;
-                const int src = __ffsll((long long)__ballot(hit)) - 1;
-                last = __shfl((int)sm.cand[r * 64 + lane].y, src, 64);
+                for (int r = 0; r < kCandMax / 64; ++r)
+                  if (r < R && ck[r] >= cand) mn = min(mn, ck[r]);
+                Pk = (uint32_t)__builtin_amdgcn_readlane(
+                    (int)f2u(wave_min(u2f(mn == 0xffffffffu ? 0x7f800000u : mn))), 63);
+                cut = true;
               }
-              run += pc;
             }
           }
+          int last = 0x7fffffff;   // with a clean cut every key == T is selected
+          int ntie = 0, need = 0;
+          if (!cut) {
+            int ngt = 0;
+#pragma unroll
+            for (int r = 0; r < kCandMax / 64; ++r)
+              if (r < R) {
+                ngt += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] > Pk));
+                ntie += (int)__popcll(__ballot(r * 64 + lane < (int)C && ck[r] == Pk));
+              }
+            need = kb - ngt;   // >= 1 elements with key Pk are taken, lowest index first
+            if (ntie != need) {
+              int run = 0;
+              last = -1;
+#pragma unroll
+              for (int r = 0; r < kCandMax / 64; ++r) {
+                if (r < R && last < 0) {
+                  const bool tie = r * 64 + lane < (int)C && ck[r] == Pk;
+                  const uint64_t m = __ballot(tie);
+                  const int pc = (int)__popcll(m);
+                  if (run + pc >= need) {
+                    const bool hit = tie && (int)lanes_below(m) == need - run - 1;
+                    const int src = __ffsll((long long)__ballot(hit)) - 1;
+                    last = __shfl((int)sm.cand[r * 64 + lane].y, src, 64);
+                  }
+                  run += pc;
+                }
+              }
+            }
+          }
+          // ring_write: the selected candidates, already in index order
           uint32_t *dst = A.G + A.row_base + off;
           int wrote = 0;
 #pragma unroll
@@ -423,7 +511,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
           if (lane == 0) {
             sm.sel[0] = Pk;
             sm.sel[1] = (uint32_t)last;
-            sm.sel[2] = (ntie == need) ? 1u : 0u;
+            sm.sel[2] = (cut || ntie == need) ? 1u : 0u;
           }
         }
         __syncthreads();
@@ -433,7 +521,11 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
         done = true;
       }
     }
-    if (!done) {
+    if (DEFER && !done) {
+      if (tid == 0) A.deferred[atomicAdd(A.n_deferred, 1u)] = j;
+      return;
+    }
+    if (!DEFER && !done) {
       // General path (k_b > 512, k_b == L, or too many candidates): exact
       // MSB-first bit search over the whole block with workgroup counts.
       uint32_t P = 0;
@@ -565,6 +657,8 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
   const uint32_t bkey = philox_block_key(A.seed, A.t, j);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
+    // keep the scheduler from interleaving chunks (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
     const int i0 = c * kChunkSpan + tid * kChunk;
     uint32_t packed = 0;
     if (!flat) {
@@ -582,7 +676,8 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
         if (i0 + e >= L) packed &= ~(15u << (4 * e));
     }
     if (ALIGNED) {
-      if (FULL || i0 < L) *reinterpret_cast<uint32_t *>(A.ef + ((s + i0) >> 1)) = packed;
+      // element s + i0 starts code word (s + i0) / 8 of the block's aligned run
+      if (FULL || i0 < L) reinterpret_cast<uint32_t *>(A.ef + (s >> 1))[c * kThreads + tid] = packed;
     } else {
       // neighbouring blocks (and threads) may share a code byte: change only
       // this element's nibble, by xor-ing old ^ new into its 32-bit word
@@ -610,16 +705,37 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
 
 // The compressor kernels: one workgroup per block.  compress_full_kernel
 // serves blocks whose every element exists and is aligned (B_d = CPT * 4096,
-// 16-byte aligned gradients): blocks 0 .. grid-1.  compress_kernel serves the
-// rest with bounds tests: blocks first_block .. first_block + grid - 1.
+// 16-byte aligned gradients): blocks first_block .. first_block + grid - 1.
+// compress_kernel serves the rest with bounds tests, over the same kind of
+// range.  A block the full kernel defers is appended to A.deferred (whose
+// count is *A.n_deferred) and finished by compress_deferred_kernel.
 template <int CPT, bool EF>
-__global__ __launch_bounds__(kThreads, 4) void compress_full_kernel(CompressArgs A) {
+__global__ __launch_bounds__(kThreads, 4) void compress_full_kernel(CompressArgs A, int64_t first_block) {
   __shared__ CompressSmem<CPT> sm;
-  const int64_t j = xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
-  const int64_t s = j * (int64_t)A.B;
-  const int64_t off = A.off_tab[j];
-  const int kb = (int)(A.off_tab[j + 1] - off);
-  compress_block<CPT, true, true, EF>(A, sm, j, s, CPT * kChunkSpan, off, kb);
+  __shared__ FullBlockStage<CPT> st;
+  const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  FullBlockInputs<CPT> in;
+  stage_full_block<CPT, EF>(A, j, st, in);
+  compress_block<CPT, true, true, EF, true>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st, &in);
+}
+
+template <int CPT, bool EF>
+__global__ __launch_bounds__(kThreads) void compress_deferred_kernel(CompressArgs A) {
+  __shared__ CompressSmem<CPT> sm;
+  __shared__ FullBlockStage<CPT> st;
+  const unsigned int n = *A.n_deferred;
+  for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
+    const int64_t j = A.deferred[q];
+    FullBlockInputs<CPT> in;
+    stage_full_block<CPT, EF>(A, j, st, in);
+    compress_block<CPT, true, true, EF, false>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st,
+                                               &in);
+    __syncthreads();
+  }
+}
+
+__global__ void zero_u32_kernel(unsigned int *p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
 template <int CPT, bool ALIGNED, bool EF>
@@ -630,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A, int6
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
   const int kb = (int)(A.off_tab[j + 1] - off);
-  compress_block<CPT, false, ALIGNED, EF>(A, sm, j, s, L, off, kb);
+  compress_block<CPT, false, ALIGNED, EF>(A, sm, j, s, L, off, kb, nullptr, nullptr);
 }
 
 // ------------------------------------------------------------------ adamstats_apply
@@ -642,15 +758,21 @@ struct ApplyArgs {
   const float *betapow;     // [2m]: beta1^r, then beta2^r, r = 0..m-1
   float *mhat, *vhat;       // MODE 2 outputs [nblocks][B]
   const int64_t *blocks;    // MODE 2 block list
-  unsigned long long *touched;   // optional: sum of touched positions
+  unsigned long long *touched;   // optional: kTouchedSlots partial sums of touched positions
   int64_t d, k, n_b;
+  int64_t first_block;      // MODE 0, 1: blocks first_block .. first_block + grid - 1
   int32_t B, m, tm, cap;    // tm = t mod m; cap = LDS slots per pass
   int32_t ent_cap;          // window entries the LDS copy holds (m*k_b must fit to use it)
   float c1, c2, lr, eps, decay;
 };
 
 enum { kModeSparse = 0, kModeDense = 1, kModeMoments = 2 };
-constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
+constexpr int kThetaPerThread = 8;
+#ifndef MA_DENSE_GROUP
+#define MA_DENSE_GROUP 1
+#endif
+constexpr int kDenseGroup = MA_DENSE_GROUP;   // threads streamed together in the dense update
+constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over   // parameters a thread holds in flight in the sparse update
 
 // MODE 0: only touched parameters are read and written (decay must be 1).
 // MODE 1: the block's parameters are streamed through registers; decoupled
@@ -674,30 +796,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   __shared__ uint32_t s_cnt[kWaves + 1];
 
   const int tid = (int)threadIdx.x;
-  const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x] : xcd_block((int64_t)blockIdx.x, A.n_b);
+  const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x]
+                                           : A.first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
   const int64_t s = j * (int64_t)A.B;
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
   const int kb = (int)(A.off_tab[j + 1] - off);
   const int M = A.m;
   const bool in_lds = M * kb <= A.ent_cap;
-
-  float th[CPT][kChunk];
-  if (MODE == kModeDense) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int i0 = c * kChunkSpan + tid * kChunk;
-      if (ALIGNED && i0 + kChunk <= L) {
-        const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
-        const float4 v1 = *reinterpret_cast<const float4 *>(A.theta + s + i0 + 4);
-        th[c][0] = v0.x; th[c][1] = v0.y; th[c][2] = v0.z; th[c][3] = v0.w;
-        th[c][4] = v1.x; th[c][5] = v1.y; th[c][6] = v1.z; th[c][7] = v1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? A.theta[s + i0 + e] : 0.f;
-      }
-    }
-  }
 
   for (int w = tid; w < W; w += kThreads) s_bits[w] = 0;
   __syncthreads();
@@ -743,14 +849,10 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
       b += wc[r];
     }
   }
-  if (MODE != kModeMoments && A.touched && tid == 0) atomicAdd(A.touched, (unsigned long long)U);
+  // spread over kTouchedSlots counters so the blocks do not contend
+  if (MODE != kModeMoments && A.touched && tid == 0)
+    atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
 
-  if (MODE == kModeDense) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-#pragma unroll
-      for (int e = 0; e < kChunk; ++e) th[c][e] = th[c][e] * A.decay;
-  }
   if (MODE == kModeMoments) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
@@ -798,6 +900,38 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
         thv[u] = (x < n) ? A.theta[s + s_pos[x]] : 0.f;
       }
     }
+    // dense: the thread's 8 consecutive parameters of each chunk, streamed
+    // when any of them is touched (or all of them in the decay pass)
+    const bool decay_pass = (MODE == kModeDense) && s0 == 0 && A.decay != 1.0f;
+    float th[CPT][kChunk];
+    uint32_t tb[CPT];
+    if (MODE == kModeDense) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int i0 = c * kChunkSpan + tid * kChunk;
+        tb[c] = (i0 < L) ? (s_bits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
+        // whole groups of kDenseGroup threads (kDenseGroup * 32 bytes) are read
+        // and written together
+        uint32_t grp = tb[c];
+        if (kDenseGroup >= 2) grp |= dpp_u32<0xb1, 0xf>(0u, grp);   // quad_perm [1,0,3,2]
+        if (kDenseGroup >= 4) grp |= dpp_u32<0x4e, 0xf>(0u, grp);   // quad_perm [2,3,0,1]
+        tb[c] |= grp ? 0x100u : 0u;   // bit 8: the group is streamed
+        if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
+          if (ALIGNED && i0 + kChunk <= L) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
+            const float4 v1 = *reinterpret_cast<const float4 *>(A.theta + s + i0 + 4);
+            th[c][0] = v0.x; th[c][1] = v0.y; th[c][2] = v0.z; th[c][3] = v0.w;
+            th[c][4] = v1.x; th[c][5] = v1.y; th[c][6] = v1.z; th[c][7] = v1.w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? A.theta[s + i0 + e] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kChunk; ++e) th[c][e] = 0.f;
+        }
+      }
+    }
     // AdamStats: z[I] += beta^r V, rows in physical order, one row at a time
     for (int i = 0; i < M; ++i) {
       int r = A.tm - i;
@@ -827,6 +961,36 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
           A.theta[s + s_pos[x]] = thv[u] - A.lr * (mh / (sqrtf(vh) + A.eps));
         }
       }
+    } else if (MODE == kModeDense) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int i0 = c * kChunkSpan + tid * kChunk;
+        if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
+          const uint32_t word = s_bits[i0 >> 5];
+          const uint32_t base = s_wbase[i0 >> 5];
+#pragma unroll
+          for (int e = 0; e < kChunk; ++e) {
+            if (decay_pass) th[c][e] = th[c][e] * A.decay;
+            if ((tb[c] >> e) & 1u) {   // e < 8: the position's own bit
+              const int bit = (i0 & 31) + e;
+              const uint32_t sl = base + (uint32_t)__popc(word & ((1u << bit) - 1u)) - s0;
+              if (sl < n) {
+                const float mh = A.c1 * s_z1[sl];
+                const float vh = A.c2 * s_z2[sl];
+                th[c][e] = th[c][e] - A.lr * (mh / (sqrtf(vh) + A.eps));
+              }
+            }
+          }
+          if (ALIGNED && i0 + kChunk <= L) {
+            *reinterpret_cast<float4 *>(A.theta + s + i0) = make_float4(th[c][0], th[c][1], th[c][2], th[c][3]);
+            *reinterpret_cast<float4 *>(A.theta + s + i0 + 4) = make_float4(th[c][4], th[c][5], th[c][6], th[c][7]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+              if (i0 + e < L) A.theta[s + i0 + e] = th[c][e];
+          }
+        }
+      }
     } else {
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
@@ -838,14 +1002,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
             if ((word >> (i & 31)) & 1u) {
               const uint32_t sl = s_wbase[i >> 5] + (uint32_t)__popc(word & ((1u << (i & 31)) - 1u)) - s0;
               if (sl < n) {
-                const float mh = A.c1 * s_z1[sl];
-                const float vh = A.c2 * s_z2[sl];
-                if (MODE == kModeDense) {
-                  th[c][e] = th[c][e] - A.lr * (mh / (sqrtf(vh) + A.eps));
-                } else {
-                  A.mhat[(int64_t)blockIdx.x * A.B + i] = mh;
-                  A.vhat[(int64_t)blockIdx.x * A.B + i] = vh;
-                }
+                A.mhat[(int64_t)blockIdx.x * A.B + i] = A.c1 * s_z1[sl];
+                A.vhat[(int64_t)blockIdx.x * A.B + i] = A.c2 * s_z2[sl];
               }
             }
           }
@@ -853,21 +1011,17 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
     }
     __syncthreads();
   }
-
-  if (MODE == kModeDense) {
+  if (MODE == kModeDense && U == 0 && A.decay != 1.0f) {
+    // nothing touched: the decay alone
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int i0 = c * kChunkSpan + tid * kChunk;
-      if (ALIGNED && i0 + kChunk <= L) {
-        *reinterpret_cast<float4 *>(A.theta + s + i0) = make_float4(th[c][0], th[c][1], th[c][2], th[c][3]);
-        *reinterpret_cast<float4 *>(A.theta + s + i0 + 4) = make_float4(th[c][4], th[c][5], th[c][6], th[c][7]);
-      } else {
 #pragma unroll
-        for (int e = 0; e < kChunk; ++e)
-          if (i0 + e < L) A.theta[s + i0 + e] = th[c][e];
-      }
+      for (int e = 0; e < kChunk; ++e)
+        if (i0 + e < L) A.theta[s + i0 + e] = A.theta[s + i0 + e] * A.decay;
     }
   }
+
 }
 
 }  // namespace microadam

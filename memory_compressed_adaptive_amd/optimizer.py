@@ -147,6 +147,11 @@ class MicroAdam:
         _L.check(_L.lib().ma_kernel_times(self._h, ms, n, 2))
         return {"compress": (ms[0], n[0]), "adamstats_apply": (ms[1], n[1])}
 
+    def set_pipeline(self, chunks: int):
+        """Number of block ranges whose update overlaps the next range's
+        compression (1 = no overlap)."""
+        _L.check(_L.lib().ma_set_pipeline(self._h, int(chunks)))
+
     def set_count_touched(self, on: bool):
         _L.check(_L.lib().ma_set_count_touched(self._h, 1 if on else 0))
 

@@ -68,7 +68,7 @@ def to_gpu_bf16(g_bits: np.ndarray, misalign: bool = False):
 
 def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0.999, eps=1e-8,
                 seed=42, flags=0, grad_fn=None, rng_seed=0, moments=True, misalign=False,
-                gpu_only_flags=0):
+                gpu_only_flags=0, chunks=None):
     """Full-state comparison after every step.  Returns the optimizer's exported
     state and the final parameters for further checks."""
     rng = np.random.default_rng(rng_seed)
@@ -76,6 +76,8 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
     theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
     opt = MicroAdam(d, B, k, m, beta1=beta1, beta2=beta2, eps=eps, lr=lr, wd=wd, seed=seed)
     opt.set_flags(flags | gpu_only_flags)
+    if chunks is not None:
+        opt.set_pipeline(chunks)
     cfg = O.make_cfg(d, B, k, m, 4, beta1, beta2, eps, lr, wd, seed, flags & O.FLAG_NO_EF)
     orc = O.FullState(cfg)
     assert opt.state_bytes() == O.state_bytes(cfg)
@@ -88,7 +90,7 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
         g = grad_fn(rng, d, t)
         g_gpu = to_gpu_bf16(g, misalign)
         say(f"[{label}] step {t}: d={d} B={B} k={k} m={m} wd={wd} flags={flags | gpu_only_flags} "
-            f"misalign={misalign}")
+            f"misalign={misalign} chunks={chunks}")
         opt.step(theta_gpu, g_gpu)
         torch.cuda.synchronize()
         mh, vh = orc.step(theta_cpu, g, moments=True)

@@ -102,6 +102,17 @@ def test_misaligned_gradient_pointer():
     full_parity("misaligned grads", 70_000, 16384, 700, 3, 4, misalign=True)
 
 
+@pytest.mark.parametrize("chunks,wd,misalign", [
+    (5, 0.0, False),      # update of range i overlaps compression of range i+1
+    (5, 0.1, False),      # dense update under the overlap
+    (3, 0.0, True),       # unaligned gradients: general compressor per range
+    (64, 0.0, False),     # more ranges than blocks: one block per range
+])
+def test_pipelined_step(chunks, wd, misalign):
+    full_parity(f"pipeline {chunks}", 200_003, 16384, 2000, 4, 5, lr=1e-2 if wd else 1e-4, wd=wd,
+                misalign=misalign, chunks=chunks)
+
+
 def test_long_window_multi_pass_slots():
     # m * k_b > LDS slots: the update kernel runs several slot passes
     full_parity("m=37 k=d/10", 40_000, 16384, 4_000, 37, 40, moments=True)
