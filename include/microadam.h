@@ -162,6 +162,8 @@ int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk);
  * the time the two kernels spend sharing the device.
  */
 int ma_set_pipeline(ma_ctx *h, int chunks);
+/* Number of block ranges ma_step uses (min(chunks, n_b)); -1 for NULL. */
+int ma_get_pipeline(const ma_ctx *h);
 
 /* Counting of touched parameters (positions present in the window, i.e. the
  * parameters an update reads and writes), summed over blocks and steps.

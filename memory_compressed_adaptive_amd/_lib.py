@@ -31,7 +31,7 @@ EXPORTS = (
     "ma_create", "ma_step", "ma_state_bytes", "ma_aux_bytes", "ma_destroy", "ma_last_error",
     "ma_last_error_message", "ma_get_step", "ma_num_blocks", "ma_set_step", "ma_set_flags",
     "ma_set_lr", "ma_read_state", "ma_write_state", "ma_debug_moments", "ma_set_timing",
-    "ma_kernel_times", "ma_set_pipeline", "ma_set_count_touched", "ma_touched_count",
+    "ma_kernel_times", "ma_set_pipeline", "ma_get_pipeline", "ma_set_count_touched", "ma_touched_count",
 )
 
 _lib = None
@@ -88,6 +88,8 @@ def lib():
     L.ma_kernel_times.argtypes = [p, p, p, C.c_int]
     L.ma_set_pipeline.restype = C.c_int
     L.ma_set_pipeline.argtypes = [p, C.c_int]
+    L.ma_get_pipeline.restype = C.c_int
+    L.ma_get_pipeline.argtypes = [p]
     L.ma_set_count_touched.restype = C.c_int
     L.ma_set_count_touched.argtypes = [p, C.c_int]
     L.ma_touched_count.restype = i64

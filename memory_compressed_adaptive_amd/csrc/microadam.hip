@@ -154,13 +154,13 @@ struct DeviceGuard {
 
 // Compressor launches for blocks [b0, b1): blocks below n_full take the
 // bounds-free kernel (plus the kernel finishing what it deferred), the rest
-// the general one.  a.deferred / a.n_deferred are this range's list.
+// the general one.  a.deferred / a.n_deferred are this range's list; its
+// counter must be zero on entry.
 template <int CPT, bool AL, bool EF>
 hipError_t launch_compress(const CompressArgs &a, int64_t b0, int64_t b1, int64_t n_full, hipStream_t s) {
   const int64_t f1 = std::min(b1, n_full);
   if (CPT <= 4 && AL && f1 > b0) {
     constexpr int C4 = CPT <= 4 ? CPT : 4;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, s, a.n_deferred, 1);
     hipLaunchKernelGGL((compress_full_kernel<C4, EF>), dim3((unsigned)(f1 - b0)), dim3(kThreads), 0, s, a, b0);
     hipLaunchKernelGGL((compress_deferred_kernel<C4, EF>), dim3((unsigned)std::min<int64_t>(f1 - b0, 256)),
                        dim3(kThreads), 0, s, a);
@@ -442,6 +442,11 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     e = hipEventRecord(h->fork_ev, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
   }
+  // every range's deferred-block counter starts at zero
+  if (e == hipSuccess && n_full > 0) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, chunks);
+    e = hipGetLastError();
+  }
   for (int i = 0; i < chunks && e == hipSuccess; ++i) {
     const int64_t b0 = h->n_b * i / chunks, b1 = h->n_b * (i + 1) / chunks;
     CompressArgs cai = ca;
@@ -588,6 +593,10 @@ int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk) {
     launches_out[i] = h->acc_n[i];
   }
   return MA_OK;
+}
+
+int ma_get_pipeline(const ma_ctx *h) {
+  return h ? (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b)) : -1;
 }
 
 int ma_set_pipeline(ma_ctx *h, int chunks) {

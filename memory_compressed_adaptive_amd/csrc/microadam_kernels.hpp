@@ -34,6 +34,9 @@ constexpr int kChunk = 8;                       // consecutive elements per thre
 constexpr int kChunkSpan = kThreads * kChunk;   // 4096 elements per chunk
 constexpr int kCandMax = 512;                   // candidates one wave selects from (8 per lane)
 constexpr int kCoarseLowBit = 16;               // candidate threshold keeps key bits 30..16
+#ifndef MA_FULL_WAVES
+#define MA_FULL_WAVES 6   // 80 VGPRs: three 512-thread blocks per CU
+#endif
 
 // ------------------------------------------------------------------ scalars
 
@@ -218,15 +221,16 @@ struct CompressSmem {
 
 // Quantization code of one element (the third paragraph's unbiased Q):
 // code = floor(y) + [u < frac(y) * 2^16], capped at 15, with y = (v - lo) * inv
-// and u the element's 16-bit uniform.  With Y = y * 2^16 (exact scaling) and
-// nu = 65535 - u this is (ceil(Y) + nu) >> 16: ceil(Y) = 2^16 floor(y) +
-// ceil(2^16 frac(y)), and ceil(2^16 frac) + 65535 - u >= 2^16 exactly when
-// 2^16 frac > u.
-__device__ __forceinline__ uint32_t quant_code(float v, float lo, float inv, uint32_t nu) {
+// and u the element's 16-bit uniform.  With xi = u * 2^-16 this is
+// min(ceil(y - xi), 15): for y >= xi the difference is exact in fp32 (y < 16
+// and xi are both multiples of ulp(y) <= 2^-16 unless u = 0, and the result
+// is below 2 ulp-binades of y), and ceil(n + f - xi) = n + [f > xi]; for
+// y < xi (so floor(y) = 0 and u > 2^16 y) it is <= 0.  Returned as a float
+// holding the integer code (or -0).
+__device__ __forceinline__ float quant_code_f(float v, float lo, float inv, uint32_t u) {
   const float y = (v - lo) * inv;
-  const float Y = y * 65536.0f;
-  const uint32_t c = (uint32_t)ceilf(Y);
-  return min((c + nu) >> 16, 15u);
+  const float z = fmaf((float)u, -1.0f / 65536.0f, y);
+  return fminf(ceilf(z), 15.0f);
 }
 
 // One block of the compressor, templated on the chunk count (CPT), on whether
@@ -317,7 +321,10 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
       const u32x4 gvc = st->g[c][tid];
       oldc[c] = cwc;
       const uint32_t gw[4] = {gvc.x, gvc.y, gvc.z, gvc.w};
-      const uint32_t ce = cwc & 0x0f0f0f0fu, co = (cwc >> 4) & 0x0f0f0f0fu;
+      // even / odd codes as bytes; the empty asm keeps the masks, so each
+      // code converts with one byte-select conversion
+      uint32_t ce = cwc & 0x0f0f0f0fu, co = (cwc >> 4) & 0x0f0f0f0fu;
+      asm volatile("" : "+v"(ce), "+v"(co));
 #pragma unroll
       for (int e = 0; e < kChunk; ++e) {
         const float gf = (e & 1) ? u2f(gw[e >> 1] & 0xffff0000u) : u2f(gw[e >> 1] << 16);
@@ -662,13 +669,16 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
     const int i0 = c * kChunkSpan + tid * kChunk;
     uint32_t packed = 0;
     if (!flat) {
+      // even elements' codes go to the bytes of ev, odd ones to od (the
+      // byte conversion saturates, so -0 becomes 0), then nibbles interleave
+      uint32_t ev = 0, od = 0;
 #pragma unroll
       for (int pr = 0; pr < kChunk / 2; ++pr) {
-        const uint32_t nh = ~pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
-        const uint32_t c0 = quant_code(a[c][2 * pr], mn, inv, nh & 0xffffu);
-        const uint32_t c1 = quant_code(a[c][2 * pr + 1], mn, inv, nh >> 16);
-        packed |= (c0 << (8 * pr)) | (c1 << (8 * pr + 4));
+        const uint32_t h = pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr], mn, inv, h & 0xffffu), pr, ev);
+        od = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr + 1], mn, inv, h >> 16), pr, od);
       }
+      packed = ev | (od << 4);
     }
     if (!FULL) {
 #pragma unroll
@@ -710,7 +720,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
 // range.  A block the full kernel defers is appended to A.deferred (whose
 // count is *A.n_deferred) and finished by compress_deferred_kernel.
 template <int CPT, bool EF>
-__global__ __launch_bounds__(kThreads, 4) void compress_full_kernel(CompressArgs A, int64_t first_block) {
+__global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void compress_full_kernel(CompressArgs A, int64_t first_block) {
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);

@@ -152,6 +152,11 @@ class MicroAdam:
         compression (1 = no overlap)."""
         _L.check(_L.lib().ma_set_pipeline(self._h, int(chunks)))
 
+    @property
+    def pipeline(self) -> int:
+        """Block ranges the step uses (1: no overlap)."""
+        return int(_L.lib().ma_get_pipeline(self._h))
+
     def set_count_touched(self, on: bool):
         _L.check(_L.lib().ma_set_count_touched(self._h, 1 if on else 0))
 
