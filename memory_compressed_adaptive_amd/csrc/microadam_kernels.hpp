@@ -222,11 +222,11 @@ struct CompressSmem {
 // Quantization code of one element (the third paragraph's unbiased Q):
 // code = floor(y) + [u < frac(y) * 2^16], capped at 15, with y = (v - lo) * inv
 // and u the element's 16-bit uniform.  With xi = u * 2^-16 this is
-// min(ceil(y - xi), 15): for y >= xi the difference is exact in fp32 (y < 16
-// and xi are both multiples of ulp(y) <= 2^-16 unless u = 0, and the result
-// is below 2 ulp-binades of y), and ceil(n + f - xi) = n + [f > xi]; for
-// y < xi (so floor(y) = 0 and u > 2^16 y) it is <= 0.  Returned as a float
-// holding the integer code (or -0).
+// min(ceil(y - xi), 15): for y >= xi the difference is exact in fp32 (y < 16,
+// so y and xi are multiples of ulp(y) <= 2^-20, and so is their difference,
+// which is at most y), and ceil(n + f - xi) = n + [f > xi]; for y < xi (so
+// floor(y) = 0 and u > 2^16 y) it is <= 0.  Returned as a float holding the
+// integer code (or -0).
 __device__ __forceinline__ float quant_code_f(float v, float lo, float inv, uint32_t u) {
   const float y = (v - lo) * inv;
   const float z = fmaf((float)u, -1.0f / 65536.0f, y);

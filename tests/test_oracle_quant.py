@@ -74,12 +74,22 @@ def test_quantizer_is_unbiased():
 
 
 def test_round_to_nearest_would_be_caught():
-    # guard for the unbiasedness pin itself: deterministic rounding of a fixed
-    # x is biased, and the test statistic above sees it
-    x = np.float64(0.3)
-    levels = np.arange(16) / 15.0
-    nearest = levels[np.argmin(np.abs(levels - x))]
-    assert abs(nearest - x) > 1e-3
+    # guard for the unbiasedness pin: the same statistic, applied to deterministic
+    # rounding rules planted in a numpy copy of the quantizer (nearest level, and
+    # always down), rejects them
+    rng = np.random.default_rng(11)
+    n, N = 4096, 3000
+    x = rng.standard_normal(n).astype(np.float32)
+    lo, hi = O.group_minmax(x)
+    s = float(_levels(lo, hi))
+    y = (x.astype(np.float64) - float(lo)) * 15.0 / (float(hi) - float(lo))
+    p = y - np.floor(y)
+    sd = s * np.sqrt(p * (1 - p))
+    for planted in (np.rint(y), np.floor(y)):
+        xh = float(lo) + np.clip(planted, 0, 15) * s
+        mean = xh - x.astype(np.float64)          # every draw gives the same value
+        z = np.abs(mean) / np.maximum(sd / np.sqrt(N), s * 2.0 ** -16)
+        assert z.max() > 6.0
 
 
 def _omega(n, lo, hi, b=4):
