@@ -61,6 +61,8 @@ enum {
 #define MA_FLAG_FORCE_DENSE 4u  /* stream the parameters in the update (same results) */
 #define MA_FLAG_FORCE_SPARSE 8u /* gather only touched parameters (same results; ignored
                                    when weight decay makes every parameter change) */
+#define MA_FLAG_UNFUSED 16u     /* run compress and update as two kernels even where the
+                                   fused per-block kernel applies (same results) */
 
 /* State buffers for ma_read_state / ma_write_state. */
 #define MA_STATE_CODES 0
@@ -142,10 +144,12 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
                      float *vhat_out, hipStream_t stream);
 
 /*
- * Per-kernel timing with HIP events recorded on the step's stream around each
- * kernel.  ma_set_timing(h, 1) clears and starts collecting; ma_kernel_times
- * waits for the recorded events and returns, for nk <= 2 kernels (0: compress,
- * 1: adamstats_apply), the summed milliseconds and launch counts.
+ * Per-kernel timing with HIP events recorded around each launch, on the stream
+ * the kernel runs on.  ma_set_timing(h, 1) clears and starts collecting;
+ * ma_kernel_times waits for the recorded events and returns, for nk <= 3
+ * kernels (0: compress, 1: adamstats_apply, 2: the fused step of full blocks,
+ * with the pass over the blocks it deferred), the summed milliseconds and
+ * launch counts.  The fused step's own launches are not counted under 0 or 1.
  */
 int ma_set_timing(ma_ctx *h, int on);
 int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk);

@@ -39,6 +39,8 @@ constexpr size_t kApplyLdsLimit = 64 * 1024;
 
 }  // namespace
 
+constexpr int kTimedKernels = 3;   // compress, adamstats_apply, fused step
+
 struct ma_ctx {
   int64_t d = 0, k = 0, n_b = 0;
   int32_t B = 0, m = 0, b = 4;
@@ -52,6 +54,7 @@ struct ma_ctx {
   int ent_cap = 0;   // window entries of one block the update kernel keeps in LDS
   bool dense_default = false;   // stream the parameters in the update even without decay
   size_t apply_lds = 0;
+  bool fused_ok = false;   // the block's window fits the fused kernel's LDS (kFusedEnt)
 
   uint8_t *codes = nullptr;
   size_t codes_bytes = 0, codes_alloc = 0;
@@ -77,8 +80,8 @@ struct ma_ctx {
   struct Ev { int kernel; hipEvent_t start, end; };
   std::vector<Ev> events;          // recorded, not yet read
   std::vector<hipEvent_t> pool;    // free timing events
-  double acc_ms[2] = {0, 0};
-  int64_t acc_n[2] = {0, 0};
+  double acc_ms[kTimedKernels] = {0, 0, 0};
+  int64_t acc_n[kTimedKernels] = {0, 0, 0};
 };
 
 namespace {
@@ -215,6 +218,29 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
   }
 }
 
+// The fused step for blocks [0, n_full): the fused kernel, then the blocks it
+// deferred (compress, then update, from the device list).
+template <int CPT, bool EF>
+hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
+  hipLaunchKernelGGL((step_full_kernel<CPT, EF>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a, (int64_t)0);
+  const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
+  hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF>), dim3(grid2), dim3(kThreads), 0, s, c);
+  ApplyArgs al = a;
+  al.blocks = c.deferred;
+  al.n_list = c.n_deferred;
+  hipLaunchKernelGGL((apply_list_kernel<CPT>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_fused(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
+                          size_t apply_lds, hipStream_t s) {
+  switch (cpt) {
+    case 1: return ef ? launch_fused<1, true>(c, a, n_full, apply_lds, s) : launch_fused<1, false>(c, a, n_full, apply_lds, s);
+    case 2: return ef ? launch_fused<2, true>(c, a, n_full, apply_lds, s) : launch_fused<2, false>(c, a, n_full, apply_lds, s);
+    default: return ef ? launch_fused<4, true>(c, a, n_full, apply_lds, s) : launch_fused<4, false>(c, a, n_full, apply_lds, s);
+  }
+}
+
 ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float decay) {
   ApplyArgs a{};
   a.G = h->window;
@@ -285,17 +311,21 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     bp[(size_t)m + r] = (float)std::pow((double)beta2, (double)r);
   }
   // The update kernel's LDS: bitmap and slot bases (8 bytes per 32 positions),
-  // the block's window entries when they fit in a quarter of the budget, and
+  // the block's window entries when they fit in 5/8 of the budget (the rows
+  // are then read from global memory once, not once per row pass), and
   // 10 bytes per slot for at most min(B_d, m*kb_max) touched positions.
   const int W = h->cpt * kChunkSpan / 32;
   const int64_t ents = (int64_t)m * kb_max;
-  h->ent_cap = (4 * ents <= (int64_t)kApplyLdsLimit / 4) ? (int)ents : 0;
+  h->ent_cap = (4 * ents <= (int64_t)kApplyLdsLimit * 5 / 8) ? (int)ents : 0;
   const int64_t umax = std::min<int64_t>((int64_t)B_d, ents);
   const int64_t cap_limit = ((int64_t)kApplyLdsLimit - 8 * (int64_t)W - 4 * (int64_t)h->ent_cap) / 10;
   h->cap = (int)std::max<int64_t>(1, std::min<int64_t>(umax, cap_limit));
   h->apply_lds = 8 * (size_t)W + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
   // expected fraction of positions present in a full window: 1 - (1 - k/d)^m
   h->dense_default = false;   // measured: gathering touched parameters wins at m = 1 and m = 10
+  // fused kernel: full 4096-element chunks, CPT <= 4, and the m window rows
+  // (padded to 64 entries each) within kFusedEnt entries of LDS
+  h->fused_ok = h->cpt <= 4 && B_d == h->cpt * kChunkSpan && (int64_t)m * ((kb_max + 63) & ~63LL) <= kFusedEnt;
   h->chunks = h->n_b >= 8192 ? 8 : 1;
 
   h->codes_bytes = (size_t)((d + 1) / 2);
@@ -367,7 +397,7 @@ int ma_set_step(ma_ctx *h, int64_t t) {
 int ma_set_flags(ma_ctx *h, uint32_t flags) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_flags: null handle");
-  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE))
+  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE | MA_FLAG_UNFUSED))
     return fail(MA_EINVAL, "ma_set_flags: unknown flag bits");
   h->flags = flags;
   return MA_OK;
@@ -434,8 +464,38 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   // `stream`.
   const int64_t n_full = (g_al && h->B == h->cpt * kChunkSpan) ? h->d / h->B : 0;
   const bool ef = !(h->flags & MA_FLAG_NO_EF);
-  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
   hipError_t e = hipSuccess;
+
+  // Fused path: every full block runs compress and update in one workgroup;
+  // a partial last block (if any) runs the two kernels after it.
+  if (h->fused_ok && n_full > 0 && mode == kModeSparse && !(h->flags & MA_FLAG_UNFUSED)) {
+    ca.deferred = h->deferred;
+    ca.n_deferred = h->n_deferred;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
+    e = hipGetLastError();
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h))))
+      return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (t0) (void)hipEventRecord(t0, stream);
+    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, ca, aa, n_full, h->apply_lds, stream);
+    if (t1) {
+      (void)hipEventRecord(t1, stream);
+      h->events.push_back({2, t0, t1});
+    }
+    if (e == hipSuccess && n_full < h->n_b) {
+      e = dispatch_compress(h->cpt, g_al, ef, ca, n_full, h->n_b, n_full, stream);
+      ApplyArgs at = aa;
+      at.first_block = n_full;
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, h->apply_lds, stream);
+    }
+    if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
+    h->t = t;
+    h->last_c1 = c1;
+    h->last_c2 = c2;
+    return MA_OK;
+  }
+
+  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
   if (chunks > 1 && !ensure_pipeline(h, chunks)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
   hipStream_t upd = chunks > 1 ? h->side : stream;
   if (chunks > 1) {
@@ -568,15 +628,18 @@ int ma_set_timing(ma_ctx *h, int on) {
     h->pool.push_back(ev.end);
   }
   h->events.clear();
-  h->acc_ms[0] = h->acc_ms[1] = 0;
-  h->acc_n[0] = h->acc_n[1] = 0;
+  for (int i = 0; i < kTimedKernels; ++i) {
+    h->acc_ms[i] = 0;
+    h->acc_n[i] = 0;
+  }
   h->timing = on != 0;
   return MA_OK;
 }
 
 int ma_kernel_times(ma_ctx *h, double *ms_out, int64_t *launches_out, int nk) {
   clear_error();
-  if (!h || !ms_out || !launches_out || nk < 0 || nk > 2) return fail(MA_EINVAL, "ma_kernel_times: bad argument");
+  if (!h || !ms_out || !launches_out || nk < 0 || nk > kTimedKernels)
+    return fail(MA_EINVAL, "ma_kernel_times: bad argument");
   DeviceGuard guard(h->device);
   for (auto &ev : h->events) {
     float ms = 0;

@@ -293,10 +293,13 @@ __device__ __forceinline__ void wait_vm_all() {
 // FULL path: st / raw hold the block's staged inputs.
 // DEFER: a block the candidate path cannot finish (too many candidates, e.g.
 // massive ties) is appended to A.deferred untouched, for the general path.
+// lds_row (optional): the window row is also written there, from index 0.
+// Returns false when the block was deferred (DEFER) and left untouched.
 template <int CPT, bool FULL, bool ALIGNED, bool EF, bool DEFER = false>
-__device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
+__device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
                                                int64_t s, int L, int64_t off, int kb,
-                                               FullBlockStage<CPT> *st, const FullBlockInputs<CPT> *raw) {
+                                               FullBlockStage<CPT> *st, const FullBlockInputs<CPT> *raw,
+                                               uint32_t *lds_row = nullptr) {
   // The thread index is passed through an empty asm statement so that, inside
   // the persistent loop, values derived from it are recomputed per block
   // instead of being hoisted out of the loop and held in (spilled) registers.
@@ -511,7 +514,11 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
               const int idx = in ? (int)sm.cand[ci].y : 0;
               const bool sel = in && (ck[r] > Pk || (ck[r] == Pk && idx <= last));
               const uint64_t m = __ballot(sel);
-              if (sel) dst[wrote + (int)lanes_below(m)] = (uint32_t)idx | (f32_to_bf16_rne(u2f(sm.cand[ci].x)) << 16);
+              if (sel) {
+                const uint32_t ent = (uint32_t)idx | (f32_to_bf16_rne(u2f(sm.cand[ci].x)) << 16);
+                dst[wrote + (int)lanes_below(m)] = ent;
+                if (lds_row) lds_row[wrote + (int)lanes_below(m)] = ent;
+              }
               wrote += (int)__popcll(m);
             }
           }
@@ -530,7 +537,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
     }
     if (DEFER && !done) {
       if (tid == 0) A.deferred[atomicAdd(A.n_deferred, 1u)] = j;
-      return;
+      return false;
     }
     if (!DEFER && !done) {
       // General path (k_b > 512, k_b == L, or too many candidates): exact
@@ -601,7 +608,9 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
           const int i = c * kChunkSpan + tid * kChunk + e;
           const float x = fabsf(a[c][e]);
           if (MA_VALID(i) && (x > u2f(T) || (x == u2f(T) && i <= idx_last))) {
-            dst[p] = (uint32_t)i | (f32_to_bf16_rne(a[c][e]) << 16);
+            const uint32_t ent = (uint32_t)i | (f32_to_bf16_rne(a[c][e]) << 16);
+            dst[p] = ent;
+            if (lds_row) lds_row[p] = ent;
             ++p;
           }
         }
@@ -609,7 +618,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
     }
   }
 
-  if (!EF) return;   // no error feedback: codes and statistics are left as they are
+  if (!EF) return true;   // no error feedback: codes and statistics are left as they are
 
   // ---------------- zero the selected entries; block min / max of the residual
   float mn = __int_as_float(0x7f800000), mx = -__int_as_float(0x7f800000);
@@ -711,6 +720,7 @@ __device__ __forceinline__ void compress_block(const CompressArgs &A, CompressSm
     A.stats[2 * j + 1] = mx;
   }
 #undef MA_VALID
+  return true;
 }
 
 // The compressor kernels: one workgroup per block.  compress_full_kernel
@@ -767,7 +777,8 @@ struct ApplyArgs {
   const int64_t *off_tab;   // [n_b + 1]
   const float *betapow;     // [2m]: beta1^r, then beta2^r, r = 0..m-1
   float *mhat, *vhat;       // MODE 2 outputs [nblocks][B]
-  const int64_t *blocks;    // MODE 2 block list
+  const int64_t *blocks;    // MODE 2 block list; the deferred-block list of apply_list_kernel
+  const unsigned int *n_list;   // apply_list_kernel: number of blocks in `blocks`
   unsigned long long *touched;   // optional: kTouchedSlots partial sums of touched positions
   int64_t d, k, n_b;
   int64_t first_block;      // MODE 0, 1: blocks first_block .. first_block + grid - 1
@@ -777,43 +788,49 @@ struct ApplyArgs {
 };
 
 enum { kModeSparse = 0, kModeDense = 1, kModeMoments = 2 };
-constexpr int kThetaPerThread = 8;
-#ifndef MA_DENSE_GROUP
-#define MA_DENSE_GROUP 1
-#endif
-constexpr int kDenseGroup = MA_DENSE_GROUP;   // threads streamed together in the dense update
-constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over   // parameters a thread holds in flight in the sparse update
+constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
+constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over
 
+// LDS of the update: bitmap of touched positions (W words), per-word slot
+// base (W words), the block's window entries (row i at ent + i * ent_stride,
+// when in_lds), and per slot z1, z2 (fp32) and its position (u16), cap slots
+// per pass; cnt holds kWaves + 1 words.
+struct ApplySmem {
+  uint32_t *bits, *wbase, *ent;
+  float *z1, *z2;
+  uint16_t *pos;
+  uint32_t *cnt;
+  int cap, ent_stride;
+  bool in_lds;
+};
+
+// The update of block j.
 // MODE 0: only touched parameters are read and written (decay must be 1).
 // MODE 1: the block's parameters are streamed through registers; decoupled
 //         decay on all, the Adam step on the touched ones.
-// MODE 2: write m_hat and v_hat of listed blocks; parameters untouched.
-//
-// LDS: bitmap of touched positions (W words), per-word slot base (W words),
-// the block's window entries (ent_cap words, when m*k_b fits), and per slot
-// z1, z2 (fp32) and its position (u16), cap slots per pass.
-template <int CPT, int MODE, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
-  extern __shared__ uint32_t smem[];
+// MODE 2: write m_hat and v_hat of the block to row out_row of the outputs;
+//         parameters untouched.
+// PRELOADED: the block's window entries are already in sm.ent.
+template <int CPT, int MODE, bool ALIGNED, bool PRELOADED>
+__device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64_t out_row, const ApplySmem &sm) {
   constexpr int W = CPT * kChunkSpan / 32;          // bitmap words
   constexpr int WPT = (W + kThreads - 1) / kThreads;
-  uint32_t *s_bits = smem;
-  uint32_t *s_wbase = smem + W;
-  uint32_t *s_ent = smem + 2 * W;
-  float *s_z1 = reinterpret_cast<float *>(s_ent + A.ent_cap);
-  float *s_z2 = s_z1 + A.cap;
-  uint16_t *s_pos = reinterpret_cast<uint16_t *>(s_z2 + A.cap);
-  __shared__ uint32_t s_cnt[kWaves + 1];
+  uint32_t *s_bits = sm.bits;
+  uint32_t *s_wbase = sm.wbase;
+  uint32_t *s_ent = sm.ent;
+  float *s_z1 = sm.z1;
+  float *s_z2 = sm.z2;
+  uint16_t *s_pos = sm.pos;
+  uint32_t *s_cnt = sm.cnt;
 
   const int tid = (int)threadIdx.x;
-  const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x]
-                                           : A.first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
   const int64_t s = j * (int64_t)A.B;
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
   const int kb = (int)(A.off_tab[j + 1] - off);
   const int M = A.m;
-  const bool in_lds = M * kb <= A.ent_cap;
+  const bool in_lds = PRELOADED || sm.in_lds;
+  const int es = PRELOADED ? sm.ent_stride : kb;   // LDS row stride of the entries
 
   for (int w = tid; w < W; w += kThreads) s_bits[w] = 0;
   __syncthreads();
@@ -822,7 +839,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   // (8 rows in flight per thread), copied to LDS when they fit; union bitmap.
   // A zero value adds nothing (unwritten rows are all zero); an index outside
   // the block (only possible in an imported state) is ignored.
-  for (int i0 = 0; i0 < M; i0 += 8) {
+  if (PRELOADED) {
+    for (int i = 0; i < M; ++i)
+      for (int q = tid; q < kb; q += kThreads) {
+        const uint32_t e = s_ent[i * es + q];
+        if ((e & 0x7fff0000u) && (int)(e & 0xffffu) < L) atomicOr(&s_bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+      }
+  }
+  for (int i0 = 0; !PRELOADED && i0 < M; i0 += 8) {
     for (int q = tid; q < kb; q += kThreads) {
       uint32_t e[8];
 #pragma unroll
@@ -831,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (i0 + u < M) {
-          if (in_lds) s_ent[(i0 + u) * kb + q] = e[u];
+          if (in_lds) s_ent[(i0 + u) * es + q] = e[u];
           if ((e[u] & 0x7fff0000u) && (int)(e[u] & 0xffffu) < L)
             atomicOr(&s_bits[(e[u] & 0xffffu) >> 5], 1u << (e[u] & 31u));
         }
@@ -870,14 +894,14 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
       for (int e = 0; e < kChunk; ++e) {
         const int i = c * kChunkSpan + tid * kChunk + e;
         if (i < L) {
-          A.mhat[(int64_t)blockIdx.x * A.B + i] = 0.f;
-          A.vhat[(int64_t)blockIdx.x * A.B + i] = 0.f;
+          A.mhat[out_row * A.B + i] = 0.f;
+          A.vhat[out_row * A.B + i] = 0.f;
         }
       }
   }
   // sparse update: slots per pass limited by what the threads hold in flight
-  const uint32_t pass = (MODE == kModeSparse) ? min((uint32_t)A.cap, (uint32_t)(kThreads * kThetaPerThread))
-                                              : (uint32_t)A.cap;
+  const uint32_t pass = (MODE == kModeSparse) ? min((uint32_t)sm.cap, (uint32_t)(kThreads * kThetaPerThread))
+                                              : (uint32_t)sm.cap;
   __syncthreads();
 
   for (uint32_t s0 = 0; s0 < U; s0 += pass) {
@@ -920,12 +944,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
       for (int c = 0; c < CPT; ++c) {
         const int i0 = c * kChunkSpan + tid * kChunk;
         tb[c] = (i0 < L) ? (s_bits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
-        // whole groups of kDenseGroup threads (kDenseGroup * 32 bytes) are read
-        // and written together
-        uint32_t grp = tb[c];
-        if (kDenseGroup >= 2) grp |= dpp_u32<0xb1, 0xf>(0u, grp);   // quad_perm [1,0,3,2]
-        if (kDenseGroup >= 4) grp |= dpp_u32<0x4e, 0xf>(0u, grp);   // quad_perm [2,3,0,1]
-        tb[c] |= grp ? 0x100u : 0u;   // bit 8: the group is streamed
+        tb[c] |= tb[c] ? 0x100u : 0u;   // bit 8: the thread's 8 parameters are streamed
         if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
           if (ALIGNED && i0 + kChunk <= L) {
             const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
@@ -948,7 +967,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
       if (r < 0) r += M;
       const float f1 = A.betapow[r], f2 = A.betapow[M + r];
       for (int q = tid; q < kb; q += kThreads) {
-        const uint32_t e = in_lds ? s_ent[i * kb + q] : A.G[(int64_t)i * A.k + off + q];
+        const uint32_t e = in_lds ? s_ent[i * es + q] : A.G[(int64_t)i * A.k + off + q];
         const uint32_t I = e & 0xffffu;
         if (!(e & 0x7fff0000u) || (int)I >= L) continue;
         const float V = bf16_bits_to_f32(e >> 16);
@@ -1012,8 +1031,8 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
             if ((word >> (i & 31)) & 1u) {
               const uint32_t sl = s_wbase[i >> 5] + (uint32_t)__popc(word & ((1u << (i & 31)) - 1u)) - s0;
               if (sl < n) {
-                A.mhat[(int64_t)blockIdx.x * A.B + i] = A.c1 * s_z1[sl];
-                A.vhat[(int64_t)blockIdx.x * A.B + i] = A.c2 * s_z2[sl];
+                A.mhat[out_row * A.B + i] = A.c1 * s_z1[sl];
+                A.vhat[out_row * A.B + i] = A.c2 * s_z2[sl];
               }
             }
           }
@@ -1031,7 +1050,109 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
         if (i0 + e < L) A.theta[s + i0 + e] = A.theta[s + i0 + e] * A.decay;
     }
   }
+}
 
+// LDS of the standalone update: dynamic, laid out as in ApplySmem.
+template <int CPT>
+__device__ __forceinline__ ApplySmem apply_smem(const ApplyArgs &A, uint32_t *smem, uint32_t *cnt, int64_t j) {
+  constexpr int W = CPT * kChunkSpan / 32;
+  ApplySmem sm;
+  sm.bits = smem;
+  sm.wbase = smem + W;
+  sm.ent = smem + 2 * W;
+  sm.z1 = reinterpret_cast<float *>(sm.ent + A.ent_cap);
+  sm.z2 = sm.z1 + A.cap;
+  sm.pos = reinterpret_cast<uint16_t *>(sm.z2 + A.cap);
+  sm.cnt = cnt;
+  sm.cap = A.cap;
+  sm.ent_stride = 0;
+  sm.in_lds = A.m * (A.off_tab[j + 1] - A.off_tab[j]) <= A.ent_cap;
+  return sm;
+}
+
+// One workgroup per block: blocks first_block .. first_block + grid - 1
+// (MODE 0, 1) or the listed blocks (MODE 2).
+template <int CPT, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t s_cnt[kWaves + 1];
+  const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x]
+                                           : A.first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  apply_block<CPT, MODE, ALIGNED, false>(A, j, (int64_t)blockIdx.x, apply_smem<CPT>(A, smem, s_cnt, j));
+}
+
+// The sparse update of the blocks in the device list A.blocks[0 .. *A.n_list).
+template <int CPT>
+__global__ __launch_bounds__(kThreads) void apply_list_kernel(ApplyArgs A) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t s_cnt[kWaves + 1];
+  const unsigned int n = *A.n_list;
+  for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
+    const int64_t j = A.blocks[q];
+    apply_block<CPT, kModeSparse, false, false>(A, j, 0, apply_smem<CPT>(A, smem, s_cnt, j));
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ fused step
+
+// Window entries the fused kernel holds in LDS: m rows of k_b entries, each
+// row padded to whole waves (64 entries).  Sized so that three workgroups of
+// the four-chunk kernel fit the 160 KiB of LDS of a CU.
+constexpr int kFusedEnt = 1984;
+
+// The whole step of one full, aligned block in one workgroup: compress (rows
+// a1-a5) and then, with the block's window in LDS, the sparse update (a6-a7).
+// The window rows the step does not write are copied to LDS by LDS-DMA while
+// the block's gradients and codes are staged; the compressor's new row goes to
+// LDS beside its global copy.  Co-resident workgroups are in different
+// phases, so the VALU-bound compressor and the memory-bound update share each
+// CU.  A block the compressor defers is left entirely (compress and update)
+// to compress_deferred_kernel and apply_list_kernel.
+template <int CPT, bool EF>
+__global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(CompressArgs C, ApplyArgs A,
+                                                                             int64_t first_block) {
+  __shared__ CompressSmem<CPT> sm;
+  __shared__ FullBlockStage<CPT> st;
+  __shared__ uint32_t ent[kFusedEnt];
+  static_assert(sizeof(FullBlockStage<CPT>) >= 8u * (CPT * kChunkSpan / 32) + 10u * 64u, "update LDS");
+  const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  FullBlockInputs<CPT> in;
+  stage_full_block<CPT, EF>(C, j, st, in);
+
+  // window rows other than row t mod m, into ent[i * es ..] (whole waves; the
+  // lanes past k_b re-read the segment's last entry into the row's padding)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int es = (in.kb + 63) & ~63;
+  if (in.kb > 0) {
+    const int wpr = es >> 6;   // wave loads per row
+    for (int w = tid >> 6; w < A.m * wpr; w += kWaves) {
+      const int i = w / wpr, q0 = (w - i * wpr) << 6;
+      if (i == A.tm) continue;
+      const int q = min(q0 + (tid & 63), in.kb - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.G + (int64_t)i * A.k + in.off + q),
+                                       (lds_void_t *)(&ent[i * es + q0]), 4, 0, 0);
+    }
+  }
+  const bool done = compress_block<CPT, true, true, EF, true>(C, sm, j, j * (int64_t)C.B, CPT * kChunkSpan, in.off,
+                                                              in.kb, &st, &in, &ent[A.tm * es]);
+  if (!done) return;
+  __syncthreads();
+
+  constexpr int W = CPT * kChunkSpan / 32;
+  ApplySmem as;
+  as.bits = reinterpret_cast<uint32_t *>(&st);
+  as.wbase = as.bits + W;
+  as.ent = ent;
+  as.z1 = reinterpret_cast<float *>(as.wbase + W);
+  as.cap = (int)((sizeof(FullBlockStage<CPT>) - 8u * W) / 10u);
+  as.z2 = as.z1 + as.cap;
+  as.pos = reinterpret_cast<uint16_t *>(as.z2 + as.cap);
+  as.cnt = sm.cnt;
+  as.ent_stride = es;
+  as.in_lds = true;
+  apply_block<CPT, kModeSparse, false, true>(A, j, 0, as);
 }
 
 }  // namespace microadam

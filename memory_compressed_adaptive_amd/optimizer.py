@@ -141,11 +141,11 @@ class MicroAdam:
         _L.check(_L.lib().ma_set_timing(self._h, 1 if on else 0))
 
     def kernel_times(self):
-        """{'compress': (ms_total, launches), 'adamstats_apply': (...)}"""
-        ms = (C.c_double * 2)()
-        n = (C.c_int64 * 2)()
-        _L.check(_L.lib().ma_kernel_times(self._h, ms, n, 2))
-        return {"compress": (ms[0], n[0]), "adamstats_apply": (ms[1], n[1])}
+        """{'compress': (ms_total, launches), 'adamstats_apply': (...), 'step_fused': (...)}"""
+        ms = (C.c_double * 3)()
+        n = (C.c_int64 * 3)()
+        _L.check(_L.lib().ma_kernel_times(self._h, ms, n, 3))
+        return {"compress": (ms[0], n[0]), "adamstats_apply": (ms[1], n[1]), "step_fused": (ms[2], n[2])}
 
     def set_pipeline(self, chunks: int):
         """Number of block ranges whose update overlaps the next range's

@@ -109,8 +109,27 @@ def test_misaligned_gradient_pointer():
     (64, 0.0, False),     # more ranges than blocks: one block per range
 ])
 def test_pipelined_step(chunks, wd, misalign):
+    # two-kernel path (the fused per-block kernel switched off)
     full_parity(f"pipeline {chunks}", 200_003, 16384, 2000, 4, 5, lr=1e-2 if wd else 1e-4, wd=wd,
-                misalign=misalign, chunks=chunks)
+                misalign=misalign, chunks=chunks, gpu_only_flags=L.MA_FLAG_UNFUSED)
+
+
+@pytest.mark.parametrize("B", [4096, 8192, 16384])
+def test_fused_step_one_two_four_chunks(B):
+    # full blocks through the fused kernel, the ragged last block through the
+    # two kernels after it
+    d = 31 * B + 1234
+    full_parity(f"fused B={B}", d, B, d // 100, 10, 12)
+
+
+def test_fused_step_with_deferred_blocks():
+    # blocks of constant gradients tie massively: the fused kernel defers them
+    # (compress and update) to the general compressor and the list update
+    def mixed(rng, d, t):
+        g = gauss_grads(rng, d, t)
+        g[16384:3 * 16384] = O.bf16_rne(np.full(2 * 16384, 1e-3, np.float32))
+        return g
+    full_parity("fused deferred", 6 * 16384, 16384, 6 * 164, 5, 6, grad_fn=mixed)
 
 
 def test_long_window_multi_pass_slots():
