@@ -175,13 +175,22 @@ def main():
     # ---------------- roofline of the dominant kernel
     # Per-kernel times are HIP events recorded on the stream each kernel runs
     # on, around every launch of the timed region.  When the update of one
-    # block range overlaps the compression of the next, both durations include
-    # the time the two kernels share the device.
-    launches = {n: kt[n][1] / K for n in kt}                     # launches per step
-    ms_step = {n: kt[n][0] / K for n in kt}                      # summed launch time per step
+    # block range overlaps the compression of the next (two-kernel path), both
+    # durations include the time the two kernels share the device.
     bytes_c = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb       # g, codes r+w, window row, stats r+w
     bytes_a = 4 * m * k + 8 * touched                           # window read, touched theta r+w
-    kern = {"compress": bytes_c, "adamstats_apply": bytes_a}
+    # Full blocks run as one fused kernel (compress + update per block) when
+    # the library takes that path; the kernels then share the bytes by blocks.
+    if kt["step_fused"][1] > 0:
+        n_full = d // B
+        f = n_full / nb
+        kern = {"step_fused": f * (bytes_c + bytes_a), "compress": (1 - f) * bytes_c,
+                "adamstats_apply": (1 - f) * bytes_a}
+    else:
+        kern = {"compress": bytes_c, "adamstats_apply": bytes_a}
+    kern = {n: b for n, b in kern.items() if kt[n][1] > 0}
+    launches = {n: kt[n][1] / K for n in kern}                  # launches per step
+    ms_step = {n: kt[n][0] / K for n in kern}                   # summed launch time per step
     dom = max(kern, key=lambda n: ms_step[n])
     bytes_launch = kern[dom] / launches[dom]
     ms_launch = kt[dom][0] / kt[dom][1]
@@ -216,6 +225,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "d": d, "B_d": B, "k": k, "m": m, "b": 4,
                    "grad_pool": P, "update": "dense" if args.dense else "sparse",
+                   "path": "fused" if "step_fused" in kern else "two-kernel",
                    "overlap_ranges": opt.pipeline, "window_filled_before_warmup": F},
         "params_per_s": round(d * steps_per_s, 1),
         "state_bytes": opt.state_bytes(),
