@@ -293,13 +293,26 @@ __device__ __forceinline__ void wait_vm_all() {
 // FULL path: st / raw hold the block's staged inputs.
 // DEFER: a block the candidate path cannot finish (too many candidates, e.g.
 // massive ties) is appended to A.deferred untouched, for the general path.
+// The fused step's window bitmap, built by the compressor's idle waves.
+struct FusedBits {
+  uint32_t *bits;          // CPT * kChunkSpan / 32 words
+  const uint32_t *ent;     // the block's window rows in LDS, row i at ent + i * es
+  int es, M, tm;
+};
+
 // lds_row (optional): the window row is also written there, from index 0.
+// lds_hash (optional, FULL only): LDS for the block's L/2 random words; while
+// wave 0 selects, the other waves fill it, and the quantizer reads it.
+// fb (optional): while wave 0 selects, the other waves build the bitmap of
+// the positions in the window rows other than row tm, and wave 0 adds the
+// positions it selects.
 // Returns false when the block was deferred (DEFER) and left untouched.
 template <int CPT, bool FULL, bool ALIGNED, bool EF, bool DEFER = false>
 __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
                                                int64_t s, int L, int64_t off, int kb,
                                                FullBlockStage<CPT> *st, const FullBlockInputs<CPT> *raw,
-                                               uint32_t *lds_row = nullptr) {
+                                               uint32_t *lds_row = nullptr, uint32_t *lds_hash = nullptr,
+                                               const FusedBits *fb = nullptr) {
   // The thread index is passed through an empty asm statement so that, inside
   // the persistent loop, values derived from it are recomputed per block
   // instead of being hoisted out of the loop and held in (spilled) registers.
@@ -377,6 +390,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   uint32_t T = 0x7f800000u;   // k_b = 0: the key of +inf, above every finite |a|
   int idx_last = -1;
   bool exact = true;
+  bool hashed = false;         // lds_hash holds the block's random words
   if (kb > 0) {
     bool done = false;
     const int q = (kb + kWaves - 1) / kWaves;
@@ -405,6 +419,10 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) tau = min(tau, sm.red[w]);
       const float tau_f = u2f(tau);
+      // the staged inputs are dead from here on: the bitmap's words are
+      // cleared (ordered before the selection by the barriers below)
+      if (fb)
+        for (int w = tid; w < CPT * kChunkSpan / 32; w += kThreads) fb->bits[w] = 0u;
       // (2) gather the candidates (key >= tau) into LDS in index order
       uint32_t cnt[CPT], pos[CPT], C;
 #pragma unroll
@@ -518,6 +536,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
                 const uint32_t ent = (uint32_t)idx | (f32_to_bf16_rne(u2f(sm.cand[ci].x)) << 16);
                 dst[wrote + (int)lanes_below(m)] = ent;
                 if (lds_row) lds_row[wrote + (int)lanes_below(m)] = ent;
+                if (fb && (ent & 0x7fff0000u)) atomicOr(&fb->bits[idx >> 5], 1u << (idx & 31));
               }
               wrote += (int)__popcll(m);
             }
@@ -527,8 +546,27 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
             sm.sel[1] = (uint32_t)last;
             sm.sel[2] = (cut || ntie == need) ? 1u : 0u;
           }
+        } else {
+          // the other waves, meanwhile: the quantizer's random words and the
+          // bitmap of the window's other rows
+          const int t7 = tid - 64;
+          if (EF && lds_hash) {
+            const uint32_t bkey = philox_block_key(A.seed, A.t, j);
+            for (int p = t7; p < L / 2; p += kThreads - 64) lds_hash[p] = pcg_hash(bkey + (uint32_t)p);
+          }
+          if (fb) {
+            for (int i = 0; i < fb->M; ++i) {
+              if (i == fb->tm) continue;
+              for (int q = t7; q < kb; q += kThreads - 64) {
+                const uint32_t e = fb->ent[i * fb->es + q];
+                if ((e & 0x7fff0000u) && (int)(e & 0xffffu) < L)
+                  atomicOr(&fb->bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+              }
+            }
+          }
         }
         __syncthreads();
+        hashed = EF && lds_hash != nullptr;
         T = sm.sel[0];
         idx_last = (int)sm.sel[1];
         exact = sm.sel[2] != 0;
@@ -670,7 +708,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   // gets code 0 everywhere.
   const float inv = (mx == mn) ? 0.f : 15.0f / (mx - mn);
   const bool flat = (mx == mn) || !(inv <= 3.402823466e38f);
-  const uint32_t bkey = philox_block_key(A.seed, A.t, j);
+  const uint32_t bkey = hashed ? 0u : philox_block_key(A.seed, A.t, j);
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     // keep the scheduler from interleaving chunks (register pressure)
@@ -681,9 +719,14 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       // even elements' codes go to the bytes of ev, odd ones to od (the
       // byte conversion saturates, so -0 becomes 0), then nibbles interleave
       uint32_t ev = 0, od = 0;
+      uint32_t hw[kChunk / 2] = {0u, 0u, 0u, 0u};
+      if (FULL && hashed) {
+        const u32x4 hv = reinterpret_cast<const u32x4 *>(lds_hash)[c * kThreads + tid];
+        hw[0] = hv.x; hw[1] = hv.y; hw[2] = hv.z; hw[3] = hv.w;
+      }
 #pragma unroll
       for (int pr = 0; pr < kChunk / 2; ++pr) {
-        const uint32_t h = pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
+        const uint32_t h = (FULL && hashed) ? hw[pr] : pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
         ev = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr], mn, inv, h & 0xffffu), pr, ev);
         od = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr + 1], mn, inv, h >> 16), pr, od);
       }
@@ -736,7 +779,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void compress_full_kernel(
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
   FullBlockInputs<CPT> in;
   stage_full_block<CPT, EF>(A, j, st, in);
-  compress_block<CPT, true, true, EF, true>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st, &in);
+  compress_block<CPT, true, true, EF, true>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st, &in,
+                                            nullptr, reinterpret_cast<uint32_t *>(&st));
 }
 
 template <int CPT, bool EF>
@@ -749,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void compress_deferred_kernel(CompressArg
     FullBlockInputs<CPT> in;
     stage_full_block<CPT, EF>(A, j, st, in);
     compress_block<CPT, true, true, EF, false>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st,
-                                               &in);
+                                               &in, nullptr, reinterpret_cast<uint32_t *>(&st));
     __syncthreads();
   }
 }
@@ -832,20 +876,16 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
   const bool in_lds = PRELOADED || sm.in_lds;
   const int es = PRELOADED ? sm.ent_stride : kb;   // LDS row stride of the entries
 
-  for (int w = tid; w < W; w += kThreads) s_bits[w] = 0;
-  __syncthreads();
+  if (!PRELOADED) {
+    for (int w = tid; w < W; w += kThreads) s_bits[w] = 0;
+    __syncthreads();
+  }
 
   // ---------------- the block's window entries: one pass over global memory
   // (8 rows in flight per thread), copied to LDS when they fit; union bitmap.
   // A zero value adds nothing (unwritten rows are all zero); an index outside
   // the block (only possible in an imported state) is ignored.
-  if (PRELOADED) {
-    for (int i = 0; i < M; ++i)
-      for (int q = tid; q < kb; q += kThreads) {
-        const uint32_t e = s_ent[i * es + q];
-        if ((e & 0x7fff0000u) && (int)(e & 0xffffu) < L) atomicOr(&s_bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
-      }
-  }
+  // (PRELOADED: the entries and the bitmap are already complete)
   for (int i0 = 0; !PRELOADED && i0 < M; i0 += 8) {
     for (int q = tid; q < kb; q += kThreads) {
       uint32_t e[8];
@@ -862,7 +902,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       }
     }
   }
-  __syncthreads();
+  if (!PRELOADED) __syncthreads();
 
   // ---------------- compact slots: slot(p) = number of touched positions below p
   uint32_t wc[WPT], mine = 0;
@@ -961,8 +1001,44 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         }
       }
     }
-    // AdamStats: z[I] += beta^r V, rows in physical order, one row at a time
-    for (int i = 0; i < M; ++i) {
+    // AdamStats: z[I] += beta^r V, rows in physical order, one row at a time.
+    // Entries in LDS with at most one per thread and row: the thread's
+    // entries of 8 rows at a time are looked up (slot, V) before the rows are
+    // added, so each row costs one read-add-write of z and a barrier.
+    if (in_lds && kb <= kThreads) {
+      for (int i0 = 0; i0 < M; i0 += 8) {
+        uint32_t slv[8];
+        float vv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          slv[u] = 0xffffffffu;
+          vv[u] = 0.f;
+          if (i0 + u < M && tid < kb) {
+            const uint32_t e = s_ent[(i0 + u) * es + tid];
+            const uint32_t I = e & 0xffffu;
+            if ((e & 0x7fff0000u) && (int)I < L) {
+              slv[u] = s_wbase[I >> 5] + (uint32_t)__popc(s_bits[I >> 5] & ((1u << (I & 31u)) - 1u)) - s0;
+              vv[u] = bf16_bits_to_f32(e >> 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u;
+          if (i < M) {
+            int r = A.tm - i;
+            if (r < 0) r += M;
+            const float f1 = A.betapow[r], f2 = A.betapow[M + r];
+            if (slv[u] < n) {
+              s_z1[slv[u]] = s_z1[slv[u]] + f1 * vv[u];
+              s_z2[slv[u]] = s_z2[slv[u]] + f2 * (vv[u] * vv[u]);
+            }
+            __syncthreads();
+          }
+        }
+      }
+    }
+    for (int i = 0; !(in_lds && kb <= kThreads) && i < M; ++i) {
       int r = A.tm - i;
       if (r < 0) r += M;
       const float f1 = A.betapow[r], f2 = A.betapow[M + r];
@@ -1115,7 +1191,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   __shared__ uint32_t ent[kFusedEnt];
-  static_assert(sizeof(FullBlockStage<CPT>) >= 8u * (CPT * kChunkSpan / 32) + 10u * 64u, "update LDS");
+  static_assert(sizeof(FullBlockStage<CPT>) >= 4u * (CPT * kChunkSpan / 2) + 8u * (CPT * kChunkSpan / 32),
+                "random words, bitmap and slot bases fit the staging space");
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
   FullBlockInputs<CPT> in;
   stage_full_block<CPT, EF>(C, j, st, in);
@@ -1135,18 +1212,28 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
                                        (lds_void_t *)(&ent[i * es + q0]), 4, 0, 0);
     }
   }
+  // LDS of the staged inputs, once they are consumed: the quantizer's random
+  // words (L/2 words), then the bitmap and slot bases; the update's per-slot
+  // arrays later reuse the random words' space
+  constexpr int W = CPT * kChunkSpan / 32;
+  uint32_t *st_words = reinterpret_cast<uint32_t *>(&st);
+  FusedBits fbits;
+  fbits.bits = st_words + CPT * kChunkSpan / 2;
+  fbits.ent = ent;
+  fbits.es = es;
+  fbits.M = A.m;
+  fbits.tm = A.tm;
   const bool done = compress_block<CPT, true, true, EF, true>(C, sm, j, j * (int64_t)C.B, CPT * kChunkSpan, in.off,
-                                                              in.kb, &st, &in, &ent[A.tm * es]);
+                                                              in.kb, &st, &in, &ent[A.tm * es], st_words, &fbits);
   if (!done) return;
   __syncthreads();
 
-  constexpr int W = CPT * kChunkSpan / 32;
   ApplySmem as;
-  as.bits = reinterpret_cast<uint32_t *>(&st);
+  as.bits = fbits.bits;
   as.wbase = as.bits + W;
   as.ent = ent;
-  as.z1 = reinterpret_cast<float *>(as.wbase + W);
-  as.cap = (int)((sizeof(FullBlockStage<CPT>) - 8u * W) / 10u);
+  as.z1 = reinterpret_cast<float *>(st_words);
+  as.cap = (int)((4u * (CPT * kChunkSpan / 2)) / 10u);
   as.z2 = as.z1 + as.cap;
   as.pos = reinterpret_cast<uint16_t *>(as.z2 + as.cap);
   as.cnt = sm.cnt;
