@@ -158,11 +158,14 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *s_red) {
 // element (chunk c, thread tid, element e) is c*4096 + tid*8 + e, i.e.
 // (chunk, wave, lane, element) lexicographic; so the exclusive prefix over
 // (c, wave) totals plus the in-wave lane prefix gives each thread the first
-// output position of its chunk-c elements.  s_cnt holds NC*kWaves + 1 words.
+// output position of its chunk-c elements.  Every wave scans the NC*kWaves
+// totals itself, so one barrier suffices.  s_cnt holds NC*kWaves words and
+// must not be written again before the next barrier.
 template <int NC>
 __device__ __forceinline__ void ordered_offsets(const uint32_t (&cnt)[NC], uint32_t (&pos)[NC],
                                                 uint32_t &total, uint32_t *s_cnt) {
   static_assert(NC * kWaves <= 64, "one wave scans the (chunk, wave) totals");
+  constexpr int n = NC * kWaves;
   const int lane = lane_id(), wv = (int)(threadIdx.x >> 6);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -171,18 +174,12 @@ __device__ __forceinline__ void ordered_offsets(const uint32_t (&cnt)[NC], uint3
     if (lane == 63) s_cnt[c * kWaves + wv] = inc;
   }
   __syncthreads();
-  if (wv == 0) {
-    constexpr int n = NC * kWaves;
-    const uint32_t v = lane < n ? s_cnt[lane] : 0u;
-    const uint32_t inc = wave_incl_scan(v);
-    if (lane < n) s_cnt[lane] = inc - v;
-    if (lane == 63) s_cnt[n] = inc;
-  }
-  __syncthreads();
+  const uint32_t v = lane < n ? s_cnt[lane] : 0u;
+  const uint32_t inc = wave_incl_scan(v);
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) pos[c] += s_cnt[c * kWaves + wv];
-  total = s_cnt[NC * kWaves];
-  __syncthreads();
+  for (int c = 0; c < NC; ++c) pos[c] += (uint32_t)__builtin_amdgcn_readlane((int)(inc - v), c * kWaves + wvu);
+  total = (uint32_t)__builtin_amdgcn_readlane((int)inc, n - 1);
 }
 
 // Blocks are handed out so that each XCD (workgroups are dealt round-robin to
