@@ -68,6 +68,8 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="blocks in the oracle sample (default: about 10000 block-steps of oracle work)")
     ap.add_argument("--dense", action="store_true", help="stream all parameters in the update")
+    ap.add_argument("--global-quant", action="store_true",
+                    help="one (delta, Delta) over all d (two compressor passes); no oracle leg")
     ap.add_argument("--chunks", type=int, default=0,
                     help="block ranges whose update overlaps the next range's compression (0: library default)")
     args = ap.parse_args()
@@ -129,8 +131,9 @@ def main():
     log(f"inputs ready: theta {4 * d / 2**30:.1f} GiB, {P} gradient steps {2 * d * P / 2**30:.1f} GiB")
 
     opt = MicroAdam(d, B, k, m)
-    if args.dense:
-        opt.set_flags(L.MA_FLAG_FORCE_DENSE)
+    flags = (L.MA_FLAG_FORCE_DENSE if args.dense else 0) | (L.MA_FLAG_GLOBAL_QUANT if args.global_quant else 0)
+    if flags:
+        opt.set_flags(flags)
     if args.chunks:
         opt.set_pipeline(args.chunks)
     nb = opt.num_blocks
@@ -142,7 +145,9 @@ def main():
     n_pre = F + W
 
     # oracle sample: initial parameters and every pooled gradient of the sampled blocks
-    cpu_leg = not args.no_cpu_baseline
+    # (the block-sampled oracle cannot follow the global quantizer: its pair
+    # depends on every block)
+    cpu_leg = not args.no_cpu_baseline and not args.global_quant
     if cpu_leg:
         want = args.cpu_blocks or max(16, 10000 // (n_pre + K))
         every = max(1, nb // max(1, want))
@@ -178,6 +183,8 @@ def main():
     # block range overlaps the compression of the next (two-kernel path), both
     # durations include the time the two kernels share the device.
     bytes_c = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb       # g, codes r+w, window row, stats r+w
+    if args.global_quant:
+        bytes_c += 2 * d + (d + 1) // 2 + 16 * nb                # second pass: g and codes again, cut
     bytes_a = 4 * m * k + 8 * touched                           # window read, touched theta r+w
     # Full blocks run as one fused kernel (compress + update per block) when
     # the library takes that path; the kernels then share the bytes by blocks.
@@ -225,6 +232,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "d": d, "B_d": B, "k": k, "m": m, "b": 4,
                    "grad_pool": P, "update": "dense" if args.dense else "sparse",
+                   "quantizer": "global" if args.global_quant else "per block",
                    "path": "fused" if "step_fused" in kern else "two-kernel",
                    "overlap_ranges": opt.pipeline, "window_filled_before_warmup": F},
         "params_per_s": round(d * steps_per_s, 1),

@@ -63,6 +63,10 @@ enum {
                                    when weight decay makes every parameter change) */
 #define MA_FLAG_UNFUSED 16u     /* run compress and update as two kernels even where the
                                    fused per-block kernel applies (same results) */
+#define MA_FLAG_GLOBAL_QUANT 32u /* one (delta, Delta) pair over all d, the literal scalar form
+                                   of the first paragraph (default: one pair per B_d block).
+                                   Costs a second pass over gradients and codes.  The pair is
+                                   stored as every block's statistics.  Ignored with NO_EF. */
 
 /* State buffers for ma_read_state / ma_write_state. */
 #define MA_STATE_CODES 0
@@ -98,8 +102,9 @@ size_t ma_state_bytes(const ma_ctx *h);
 
 /* Everything else the library holds on the device: per-block statistics
  * (8*n_b), the block offset table (8*(n_b+1)), the beta-power table (8*m),
- * the code buffer's tail padding, the touched-parameter counters (8 KiB) and the
- * compressor's deferred-block list (8*n_b + 256).
+ * the code buffer's tail padding, the touched-parameter counters (8 KiB), the
+ * compressor's deferred-block list (8*n_b + 256) and the global quantizer's
+ * per-block min / max and cut (16*n_b + 8).
  * 0 for NULL. */
 size_t ma_aux_bytes(const ma_ctx *h);
 

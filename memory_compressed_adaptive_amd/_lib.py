@@ -22,6 +22,7 @@ MA_FLAG_NO_EF = 1
 MA_FLAG_FORCE_DENSE = 4
 MA_FLAG_FORCE_SPARSE = 8
 MA_FLAG_UNFUSED = 16
+MA_FLAG_GLOBAL_QUANT = 32
 
 MA_STATE_CODES = 0
 MA_STATE_STATS = 1

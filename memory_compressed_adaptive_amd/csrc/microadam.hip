@@ -66,6 +66,10 @@ struct ma_ctx {
   bool count_touched = false;
   int64_t *deferred = nullptr;        // blocks handed from the full-block to the general compressor
   unsigned int *n_deferred = nullptr;
+  // global quantizer (MA_FLAG_GLOBAL_QUANT): per-block min / max and cut, global pair
+  float *blkmm = nullptr;
+  uint32_t *selinfo = nullptr;
+  float *gmm = nullptr;
 
   // last step's constants (for ma_debug_moments)
   float last_c1 = 0, last_c2 = 0;
@@ -96,6 +100,9 @@ void free_all(ma_ctx *h) {
   hipFree(h->touched);
   hipFree(h->deferred);
   hipFree(h->n_deferred);
+  hipFree(h->blkmm);
+  hipFree(h->selinfo);
+  hipFree(h->gmm);
   for (auto &ev : h->events) {
     hipEventDestroy(ev.start);
     hipEventDestroy(ev.end);
@@ -241,6 +248,44 @@ hipError_t dispatch_fused(int cpt, bool ef, const CompressArgs &c, const ApplyAr
   }
 }
 
+// The global quantizer's launches over all blocks: pass 1 (full aligned
+// blocks [0, n_full) by the staged kernel, the blocks it defers, then the
+// rest), the global min / max, pass 2 (error feedback on).  a.n_deferred
+// must be zero on entry.
+template <int CPT, bool AL, int QMODE>
+void launch_global_pass(const CompressArgs &a, int64_t n_b, int64_t n_full, hipStream_t s) {
+  const dim3 blk(kThreads);
+  if (CPT <= 4 && AL && n_full > 0) {
+    constexpr int C4 = CPT <= 4 ? CPT : 4;
+    hipLaunchKernelGGL((compress_full_kernel<C4, true, QMODE>), dim3((unsigned)n_full), blk, 0, s, a, (int64_t)0);
+    if (QMODE == kQGlobal1)
+      hipLaunchKernelGGL((compress_deferred_kernel<C4, true, QMODE>), dim3((unsigned)std::min<int64_t>(n_full, 256)),
+                         blk, 0, s, a);
+  }
+  const int64_t g0 = (CPT <= 4 && AL) ? n_full : 0;
+  if (n_b > g0)
+    hipLaunchKernelGGL((compress_kernel<CPT, AL, true, QMODE>), dim3((unsigned)(n_b - g0)), blk, 0, s, a, g0);
+}
+
+template <int CPT, bool AL>
+hipError_t launch_global_q(const CompressArgs &a, int64_t n_b, int64_t n_full, hipStream_t s) {
+  launch_global_pass<CPT, AL, kQGlobal1>(a, n_b, n_full, s);
+  hipLaunchKernelGGL(global_minmax_kernel, dim3(1), dim3(kThreads), 0, s, (const float *)a.blkmm, n_b,
+                     (float *)a.gmm);
+  launch_global_pass<CPT, AL, kQGlobal2>(a, n_b, n_full, s);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_global_q(int cpt, bool aligned, const CompressArgs &a, int64_t n_b, int64_t n_full,
+                             hipStream_t s) {
+  switch (cpt) {
+    case 1: return aligned ? launch_global_q<1, true>(a, n_b, n_full, s) : launch_global_q<1, false>(a, n_b, n_full, s);
+    case 2: return aligned ? launch_global_q<2, true>(a, n_b, n_full, s) : launch_global_q<2, false>(a, n_b, n_full, s);
+    case 4: return aligned ? launch_global_q<4, true>(a, n_b, n_full, s) : launch_global_q<4, false>(a, n_b, n_full, s);
+    default: return aligned ? launch_global_q<8, true>(a, n_b, 0, s) : launch_global_q<8, false>(a, n_b, 0, s);
+  }
+}
+
 ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float decay) {
   ApplyArgs a{};
   a.G = h->window;
@@ -339,7 +384,10 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
             hipMalloc(&h->betapow, 4 * bp.size()) == hipSuccess &&
             hipMalloc(&h->touched, kTouchedSlots * sizeof(unsigned long long)) == hipSuccess &&
             hipMalloc(&h->deferred, 8 * (size_t)h->n_b) == hipSuccess &&
-            hipMalloc(&h->n_deferred, 64 * sizeof(unsigned int)) == hipSuccess;
+            hipMalloc(&h->n_deferred, 64 * sizeof(unsigned int)) == hipSuccess &&
+            hipMalloc(&h->blkmm, 8 * (size_t)h->n_b) == hipSuccess &&
+            hipMalloc(&h->selinfo, 8 * (size_t)h->n_b) == hipSuccess &&
+            hipMalloc(&h->gmm, 8) == hipSuccess;
   if (!ok) {
     (void)hipGetLastError();
     free_all(h);
@@ -381,7 +429,7 @@ size_t ma_aux_bytes(const ma_ctx *h) {
   if (!h) return 0;
   return 8 * (size_t)h->n_b + 8 * ((size_t)h->n_b + 1) + 8 * (size_t)h->m +
          (h->codes_alloc - h->codes_bytes) + kTouchedSlots * sizeof(unsigned long long) +
-         8 * (size_t)h->n_b + 64 * sizeof(unsigned int);
+         8 * (size_t)h->n_b + 64 * sizeof(unsigned int) + 16 * (size_t)h->n_b + 8;
 }
 
 int64_t ma_get_step(const ma_ctx *h) { return h ? h->t : -1; }
@@ -397,7 +445,7 @@ int ma_set_step(ma_ctx *h, int64_t t) {
 int ma_set_flags(ma_ctx *h, uint32_t flags) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_flags: null handle");
-  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE | MA_FLAG_UNFUSED))
+  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE | MA_FLAG_UNFUSED | MA_FLAG_GLOBAL_QUANT))
     return fail(MA_EINVAL, "ma_set_flags: unknown flag bits");
   h->flags = flags;
   return MA_OK;
@@ -465,6 +513,36 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   const int64_t n_full = (g_al && h->B == h->cpt * kChunkSpan) ? h->d / h->B : 0;
   const bool ef = !(h->flags & MA_FLAG_NO_EF);
   hipError_t e = hipSuccess;
+
+  // Global quantizer: the compressor in two passes around a global min / max,
+  // then the update; all on the caller's stream.
+  if (ef && (h->flags & MA_FLAG_GLOBAL_QUANT)) {
+    ca.blkmm = h->blkmm;
+    ca.selinfo = h->selinfo;
+    ca.gmm = h->gmm;
+    hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr;
+    if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h)) || !(t2 = timing_event(h)) ||
+                      !(t3 = timing_event(h))))
+      return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    ca.deferred = h->deferred;
+    ca.n_deferred = h->n_deferred;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
+    if (t0) (void)hipEventRecord(t0, stream);
+    e = dispatch_global_q(h->cpt, g_al, ca, h->n_b, n_full, stream);
+    if (t1) (void)hipEventRecord(t1, stream);
+    if (t2) (void)hipEventRecord(t2, stream);
+    if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream);
+    if (t3) {
+      (void)hipEventRecord(t3, stream);
+      h->events.push_back({0, t0, t1});
+      h->events.push_back({1, t2, t3});
+    }
+    if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
+    h->t = t;
+    h->last_c1 = c1;
+    h->last_c2 = c2;
+    return MA_OK;
+  }
 
   // Fused path: every full block runs compress and update in one workgroup;
   // a partial last block (if any) runs the two kernels after it.

@@ -205,7 +205,18 @@ struct CompressArgs {
   int32_t B;
   int64_t *deferred;        // blocks the full-block kernel hands to the general path
   unsigned int *n_deferred; // their count
+  // one (delta, Delta) over all d (two passes, QMODE 1 and 2)
+  float *blkmm;             // [2*n_b] each block's residual min / max (pass 1)
+  uint32_t *selinfo;        // [2*n_b] each block's cut: T, idx_last (0x7fffffff: every key T taken)
+  const float *gmm;         // [2] the reduced global min / max (pass 2)
 };
+
+// Quantizer modes of the compressor: per block (0), or one pair over all d:
+// pass 1 selects, writes the window row and records the block's residual
+// min / max and its cut, leaving codes and statistics; pass 2 recomputes the
+// residual from the same inputs, zeroes by the recorded cut and quantizes with
+// the global pair (which it stores as every block's statistics).
+enum { kQBlock = 0, kQGlobal1 = 1, kQGlobal2 = 2 };
 
 template <int CPT>
 struct CompressSmem {
@@ -304,7 +315,7 @@ struct FusedBits {
 // the positions in the window rows other than row tm, and wave 0 adds the
 // positions it selects.
 // Returns false when the block was deferred (DEFER) and left untouched.
-template <int CPT, bool FULL, bool ALIGNED, bool EF, bool DEFER = false>
+template <int CPT, bool FULL, bool ALIGNED, bool EF, bool DEFER = false, int QMODE = kQBlock>
 __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSmem<CPT> &sm, int64_t j,
                                                int64_t s, int L, int64_t off, int kb,
                                                FullBlockStage<CPT> *st, const FullBlockInputs<CPT> *raw,
@@ -388,7 +399,11 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   int idx_last = -1;
   bool exact = true;
   bool hashed = false;         // lds_hash holds the block's random words
-  if (kb > 0) {
+  if (QMODE == kQGlobal2) {
+    T = A.selinfo[2 * j];
+    idx_last = (int)A.selinfo[2 * j + 1];
+    exact = idx_last == 0x7fffffff;
+  } else if (kb > 0) {
     bool done = false;
     const int q = (kb + kWaves - 1) / kWaves;
     if (q <= 64 && kb < L) {
@@ -547,7 +562,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
           // the other waves, meanwhile: the quantizer's random words and the
           // bitmap of the window's other rows
           const int t7 = tid - 64;
-          if (EF && lds_hash) {
+          if (EF && QMODE == kQBlock && lds_hash) {
             const uint32_t bkey = philox_block_key(A.seed, A.t, j);
             for (int p = t7; p < L / 2; p += kThreads - 64) lds_hash[p] = pcg_hash(bkey + (uint32_t)p);
           }
@@ -563,7 +578,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
           }
         }
         __syncthreads();
-        hashed = EF && lds_hash != nullptr;
+        hashed = EF && QMODE == kQBlock && lds_hash != nullptr;
         T = sm.sel[0];
         idx_last = (int)sm.sel[1];
         exact = sm.sel[2] != 0;
@@ -699,6 +714,19 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   }
   mn = mn + 0.0f;   // a zero extreme is stored as +0
   mx = mx + 0.0f;
+  if (QMODE == kQGlobal1) {
+    if (tid == 0) {
+      A.blkmm[2 * j] = mn;
+      A.blkmm[2 * j + 1] = mx;
+      A.selinfo[2 * j] = T;
+      A.selinfo[2 * j + 1] = exact ? 0x7fffffffu : (uint32_t)idx_last;
+    }
+    return true;
+  }
+  if (QMODE == kQGlobal2) {
+    mn = A.gmm[0];
+    mx = A.gmm[1];
+  }
 
   // ---------------- ef_requant: unbiased stochastic 4-bit rounding.  A
   // constant block, or one whose scale 15/(Delta - delta) overflows fp32,
@@ -769,18 +797,19 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 // compress_kernel serves the rest with bounds tests, over the same kind of
 // range.  A block the full kernel defers is appended to A.deferred (whose
 // count is *A.n_deferred) and finished by compress_deferred_kernel.
-template <int CPT, bool EF>
+template <int CPT, bool EF, int QMODE = kQBlock>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void compress_full_kernel(CompressArgs A, int64_t first_block) {
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
   FullBlockInputs<CPT> in;
   stage_full_block<CPT, EF>(A, j, st, in);
-  compress_block<CPT, true, true, EF, true>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st, &in,
-                                            nullptr, reinterpret_cast<uint32_t *>(&st));
+  compress_block<CPT, true, true, EF, QMODE != kQGlobal2, QMODE>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off,
+                                                               in.kb, &st, &in, nullptr,
+                                                               reinterpret_cast<uint32_t *>(&st));
 }
 
-template <int CPT, bool EF>
+template <int CPT, bool EF, int QMODE = kQBlock>
 __global__ __launch_bounds__(kThreads) void compress_deferred_kernel(CompressArgs A) {
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
@@ -789,8 +818,8 @@ __global__ __launch_bounds__(kThreads) void compress_deferred_kernel(CompressArg
     const int64_t j = A.deferred[q];
     FullBlockInputs<CPT> in;
     stage_full_block<CPT, EF>(A, j, st, in);
-    compress_block<CPT, true, true, EF, false>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb, &st,
-                                               &in, nullptr, reinterpret_cast<uint32_t *>(&st));
+    compress_block<CPT, true, true, EF, false, QMODE>(A, sm, j, j * (int64_t)A.B, CPT * kChunkSpan, in.off, in.kb,
+                                                      &st, &in, nullptr, reinterpret_cast<uint32_t *>(&st));
     __syncthreads();
   }
 }
@@ -799,7 +828,7 @@ __global__ void zero_u32_kernel(unsigned int *p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
-template <int CPT, bool ALIGNED, bool EF>
+template <int CPT, bool ALIGNED, bool EF, int QMODE = kQBlock>
 __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A, int64_t first_block) {
   __shared__ CompressSmem<CPT> sm;
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
@@ -807,7 +836,34 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs A, int6
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
   const int kb = (int)(A.off_tab[j + 1] - off);
-  compress_block<CPT, false, ALIGNED, EF>(A, sm, j, s, L, off, kb, nullptr, nullptr);
+  compress_block<CPT, false, ALIGNED, EF, false, QMODE>(A, sm, j, s, L, off, kb, nullptr, nullptr);
+}
+
+// The global residual min / max from the blocks' (pass 1 to pass 2 of the
+// global quantizer): one workgroup; min and max are exact, so the order of
+// reduction does not matter; a zero extreme is stored as +0.
+__global__ __launch_bounds__(kThreads) void global_minmax_kernel(const float *blkmm, int64_t n_b, float *gmm) {
+  __shared__ float red[2 * kWaves];
+  float mn = __int_as_float(0x7f800000), mx = -__int_as_float(0x7f800000);
+  for (int64_t j = threadIdx.x; j < n_b; j += kThreads) {
+    mn = fminf(mn, blkmm[2 * j]);
+    mx = fmaxf(mx, blkmm[2 * j + 1]);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const int wv = (int)(threadIdx.x >> 6);
+  if (lane_id() == 0) { red[wv] = mn; red[kWaves + wv] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kWaves; ++w) {
+      mn = fminf(mn, red[w]);
+      mx = fmaxf(mx, red[kWaves + w]);
+    }
+    mn = fminf(mn, red[0]);
+    mx = fmaxf(mx, red[kWaves]);
+    gmm[0] = mn + 0.0f;
+    gmm[1] = mx + 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ adamstats_apply

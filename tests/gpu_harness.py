@@ -68,17 +68,18 @@ def to_gpu_bf16(g_bits: np.ndarray, misalign: bool = False):
 
 def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0.999, eps=1e-8,
                 seed=42, flags=0, grad_fn=None, rng_seed=0, moments=True, misalign=False,
-                gpu_only_flags=0, chunks=None):
+                gpu_only_flags=0, chunks=None, global_quant=False):
     """Full-state comparison after every step.  Returns the optimizer's exported
     state and the final parameters for further checks."""
     rng = np.random.default_rng(rng_seed)
     grad_fn = grad_fn or gauss_grads
     theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
     opt = MicroAdam(d, B, k, m, beta1=beta1, beta2=beta2, eps=eps, lr=lr, wd=wd, seed=seed)
-    opt.set_flags(flags | gpu_only_flags)
+    opt.set_flags(flags | gpu_only_flags | (L.MA_FLAG_GLOBAL_QUANT if global_quant else 0))
     if chunks is not None:
         opt.set_pipeline(chunks)
-    cfg = O.make_cfg(d, B, k, m, 4, beta1, beta2, eps, lr, wd, seed, flags & O.FLAG_NO_EF)
+    cfg = O.make_cfg(d, B, k, m, 4, beta1, beta2, eps, lr, wd, seed,
+                     (flags & O.FLAG_NO_EF) | (O.FLAG_GLOBAL_QUANT if global_quant else 0))
     orc = O.FullState(cfg)
     assert opt.state_bytes() == O.state_bytes(cfg)
     theta_gpu = torch.from_numpy(theta0.copy()).cuda()
@@ -97,7 +98,12 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
         assert opt.t == orc.t == t
         assert_bits_equal(f"{label} t={t} window", opt.window(), orc.G)
         assert_bits_equal(f"{label} t={t} codes", opt.codes_bytes(), orc.ef)
-        assert_bits_equal(f"{label} t={t} stats", opt.stats().view(np.uint32), orc.stats.view(np.uint32))
+        if global_quant:
+            # the one pair is stored as every block's statistics
+            gs = opt.stats().reshape(-1, 2).view(np.uint32)
+            assert_bits_equal(f"{label} t={t} stats", gs, np.broadcast_to(orc.stats.view(np.uint32), gs.shape))
+        else:
+            assert_bits_equal(f"{label} t={t} stats", opt.stats().view(np.uint32), orc.stats.view(np.uint32))
         nonbitwise += assert_close_f32(f"{label} t={t} theta", theta_gpu.cpu().numpy(), theta_cpu)
         if moments:
             gm, gv = opt.moments(mblocks)

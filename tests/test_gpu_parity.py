@@ -132,6 +132,43 @@ def test_fused_step_with_deferred_blocks():
     full_parity("fused deferred", 6 * 16384, 16384, 6 * 164, 5, 6, grad_fn=mixed)
 
 
+@pytest.mark.parametrize("d,B,k,m,misalign", [
+    (100_003, 16384, 1000, 4, False),   # full blocks and a ragged last block
+    (50_001, 8192, 2000, 3, True),      # unaligned gradients, odd d
+    (7, 3, 2, 2, False),                # every block partial
+])
+def test_global_quantizer(d, B, k, m, misalign):
+    # one (delta, Delta) over all d: pass 1, global min / max, pass 2
+    full_parity(f"global Q d={d} B={B}", d, B, k, m, 6, misalign=misalign, global_quant=True)
+
+
+def test_global_quantizer_with_deferred_blocks():
+    # tie-heavy blocks leave the staged first pass for the general selection
+    def mixed(rng, d, t):
+        g = gauss_grads(rng, d, t)
+        g[16384:3 * 16384] = O.bf16_rne(np.full(2 * 16384, 1e-3, np.float32))
+        return g
+    full_parity("global Q deferred", 6 * 16384, 16384, 6 * 164, 4, 5, grad_fn=mixed, global_quant=True)
+
+
+def test_global_quantizer_single_block_equals_block_mode():
+    # with one block the global pair is the block's pair: both modes give the same bits
+    d, B, k, m = 12_000, 16384, 120, 3
+    outs = []
+    for gq in (False, True):
+        rng = np.random.default_rng(5)
+        theta = torch.from_numpy((rng.standard_normal(d) * 0.02).astype(np.float32)).cuda()
+        opt = MicroAdam(d, B, k, m)
+        if gq:
+            opt.set_flags(L.MA_FLAG_GLOBAL_QUANT)
+        for t in range(1, 5):
+            opt.step(theta, to_gpu_bf16(gauss_grads(rng, d, t)))
+        torch.cuda.synchronize()
+        outs.append((theta.cpu().numpy(), opt.codes_bytes(), opt.stats(), opt.window()))
+    for a, b in zip(*outs):
+        assert_bits_equal("block vs global, one block", a, b)
+
+
 def test_long_window_multi_pass_slots():
     # m * k_b > LDS slots: the update kernel runs several slot passes
     full_parity("m=37 k=d/10", 40_000, 16384, 4_000, 37, 40, moments=True)

@@ -252,6 +252,23 @@ def test_global_quantizer_lemma1():
     assert err <= omega * np.linalg.norm(a.astype(np.float64))
 
 
+def test_global_quantizer_with_one_block_is_block_quantizer():
+    # d <= B_d: the pair over all d is the block's pair, so both readings agree
+    rng = np.random.default_rng(31)
+    d = 5000
+    runs = []
+    for flags in (0, O.FLAG_GLOBAL_QUANT):
+        cfg = O.make_cfg(d, 8192, d // 100, 3, flags=flags)
+        st = O.FullState(cfg)
+        theta = (np.random.default_rng(3).standard_normal(d) * 0.02).astype(np.float32)
+        r = np.random.default_rng(4)
+        for t in range(1, 5):
+            st.step(theta, _grads(r, d))
+        runs.append((theta, st.ef.copy(), st.stats.copy(), st.G.copy()))
+    for a, b in zip(*runs):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+
+
 def test_state_bytes_and_memory_paragraph():
     with open(os.path.join(GOLDEN, "microadam_memory_paragraph.json")) as f:
         page = json.load(f)
