@@ -68,6 +68,9 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=0,
                     help="blocks in the oracle sample (default: about 10000 block-steps of oracle work)")
     ap.add_argument("--dense", action="store_true", help="stream all parameters in the update")
+    ap.add_argument("--bf16-params", action="store_true",
+                    help="bfloat16 parameters (ma_step_bf16): the one-40-GB-GPU regime")
+    ap.add_argument("--wd", type=float, default=0.0, help="decoupled weight decay (dense update)")
     ap.add_argument("--global-quant", action="store_true",
                     help="one (delta, Delta) over all d (two compressor passes); no oracle leg")
     ap.add_argument("--chunks", type=int, default=0,
@@ -116,6 +119,11 @@ def main():
     # ---------------- inputs resident in HBM
     theta = torch.empty(d, dtype=torch.float32, device=dev)
     synth.fill_params(theta)
+    if args.bf16_params:
+        # bfloat16 parameters: the seeded fp32 values rounded to nearest even
+        theta = theta.to(torch.bfloat16).view(torch.int16)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     gsrc = synth.GradSource(w)
     free, _ = torch.cuda.mem_get_info()
     state_est = (d + 1) // 2 + 4 * m * k + 64 * (d // B + 1)
@@ -130,7 +138,7 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready: theta {4 * d / 2**30:.1f} GiB, {P} gradient steps {2 * d * P / 2**30:.1f} GiB")
 
-    opt = MicroAdam(d, B, k, m)
+    opt = MicroAdam(d, B, k, m, wd=args.wd)
     flags = (L.MA_FLAG_FORCE_DENSE if args.dense else 0) | (L.MA_FLAG_GLOBAL_QUANT if args.global_quant else 0)
     if flags:
         opt.set_flags(flags)
@@ -155,6 +163,8 @@ def main():
         ranges = [(int(j) * B, min(B, d - int(j) * B)) for j in blocks]
         idx = torch.from_numpy(np.concatenate([np.arange(s, s + n) for s, n in ranges])).to(dev)
         th0 = theta.index_select(0, idx).cpu().numpy()
+        if args.bf16_params:
+            th0 = th0.view(np.uint16)
         g_host = [g.index_select(0, idx).cpu().numpy().view(np.uint16) for g in pool]
 
     # ---------------- fill the window, warmup, then exactly K timed steps
@@ -185,7 +195,11 @@ def main():
     bytes_c = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb       # g, codes r+w, window row, stats r+w
     if args.global_quant:
         bytes_c += 2 * d + (d + 1) // 2 + 16 * nb                # second pass: g and codes again, cut
-    bytes_a = 4 * m * k + 8 * touched                           # window read, touched theta r+w
+    pb = 2 if args.bf16_params else 4                            # bytes per parameter
+    if args.wd:
+        bytes_a = 4 * m * k + 2 * pb * d                        # window read, every parameter r+w
+    else:
+        bytes_a = 4 * m * k + 2 * pb * touched                  # window read, touched parameters r+w
     # Full blocks run as one fused kernel (compress + update per block) when
     # the library takes that path; the kernels then share the bytes by blocks.
     if kt["step_fused"][1] > 0:
@@ -233,10 +247,13 @@ def main():
         "config": {"workload": w.name, "d": d, "B_d": B, "k": k, "m": m, "b": 4,
                    "grad_pool": P, "update": "dense" if args.dense else "sparse",
                    "quantizer": "global" if args.global_quant else "per block",
+                   "params": "bf16" if args.bf16_params else "f32", "wd": args.wd,
                    "path": "fused" if "step_fused" in kern else "two-kernel",
                    "overlap_ranges": opt.pipeline, "window_filled_before_warmup": F},
         "params_per_s": round(d * steps_per_s, 1),
         "state_bytes": opt.state_bytes(),
+        "resident_bytes": {"params": pb * d, "grads_one_step": 2 * d, "state": opt.state_bytes(),
+                           "aux": opt.aux_bytes()},
         "hbm": hbm,
         "roofline": roofline,
     }
@@ -246,8 +263,10 @@ def main():
         import oracle as O
         log(f"oracle on {len(blocks)} sampled blocks x {n_pre + K} steps ...")
         th_gpu = theta.index_select(0, idx).cpu().numpy()
+        if args.bf16_params:
+            th_gpu = th_gpu.view(np.uint16)
         stats_gpu = opt.stats()
-        cfg = O.make_cfg(d, B, k, m)
+        cfg = O.make_cfg(d, B, k, m, wd=args.wd)
         states = {int(j): O.BlockState.zeros(cfg, int(j)) for j in blocks}
         ths = []
         pos = 0
@@ -259,7 +278,13 @@ def main():
             gh = g_host[s % P]
             pos = 0
             for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
-                states[int(j)].step(ths[q], gh[pos:pos + n])
+                if args.bf16_params:
+                    # widen, fp32 step, round to nearest even once
+                    th32 = O.bf16_to_f32(ths[q]).astype(np.float32)
+                    states[int(j)].step(th32, gh[pos:pos + n])
+                    ths[q] = O.bf16_rne(th32)
+                else:
+                    states[int(j)].step(ths[q], gh[pos:pos + n])
                 pos += n
         c1 = time.perf_counter()
         per_block_step = (c1 - c0) / (len(blocks) * (n_pre + K))
@@ -279,8 +304,12 @@ def main():
             got = th_gpu[pos:pos + n]
             ref = ths[q]
             pos += n
-            same = got.view(np.uint32) == ref.view(np.uint32)
-            close = np.abs(got.astype(np.float64) - ref) <= 1e-6 * np.maximum(np.abs(ref), 1e-30)
+            if args.bf16_params:
+                same = got == ref
+                close = same
+            else:
+                same = got.view(np.uint32) == ref.view(np.uint32)
+                close = np.abs(got.astype(np.float64) - ref) <= 1e-6 * np.maximum(np.abs(ref), 1e-30)
             bad["theta"] += int((~(same | close)).sum())
             nonbitwise += int((~same).sum())
             codes = O.unpack_nibbles(opt.codes_bytes(s0 >> 1, ((s0 & 1) + n + 1) // 2), n, s0 & 1)

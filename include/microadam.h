@@ -96,6 +96,17 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
  */
 int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream);
 
+/*
+ * The same step for bfloat16 parameters (the regime of the fourth paragraph's
+ * full fine-tuning of LLaMA-2 7B on one 40 GB GPU: bf16 parameters and
+ * gradients plus 0.9d of state).  params: caller-owned device bf16[d] (raw
+ * bits), 2-byte aligned, updated in place: each changed parameter is widened
+ * exactly to fp32, updated as ma_step updates an fp32 parameter (decay, then
+ * the Adam step), and rounded to nearest even once.  Parameters no window
+ * entry touches are unchanged when wd = 0.  Errors as ma_step.
+ */
+int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream);
+
 /* Optimizer-state bytes the second paragraph of the MicroAdam page counts:
  * ceil(d/2) + 4*m*k (0.9d at m = 10, k = d/100).  0 for NULL. */
 size_t ma_state_bytes(const ma_ctx *h);

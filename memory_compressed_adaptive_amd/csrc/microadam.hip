@@ -201,51 +201,59 @@ hipError_t dispatch_compress(int cpt, bool aligned, bool ef, const CompressArgs 
   }
 }
 
-template <int CPT, int MODE, bool AL>
+template <int CPT, int MODE, bool AL, bool BF>
 hipError_t launch_apply(const ApplyArgs &a, int64_t grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((apply_kernel<CPT, MODE, AL>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((apply_kernel<CPT, MODE, AL, BF>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-template <int CPT>
+template <int CPT, bool BF>
 hipError_t launch_apply_cpt(int mode, bool aligned, const ApplyArgs &a, int64_t grid, size_t lds, hipStream_t s) {
-  if (mode == kModeSparse) return launch_apply<CPT, kModeSparse, false>(a, grid, lds, s);
-  if (mode == kModeMoments) return launch_apply<CPT, kModeMoments, false>(a, grid, lds, s);
-  return aligned ? launch_apply<CPT, kModeDense, true>(a, grid, lds, s)
-                 : launch_apply<CPT, kModeDense, false>(a, grid, lds, s);
+  if (mode == kModeSparse) return launch_apply<CPT, kModeSparse, false, BF>(a, grid, lds, s);
+  if (mode == kModeMoments) return launch_apply<CPT, kModeMoments, false, false>(a, grid, lds, s);
+  return aligned ? launch_apply<CPT, kModeDense, true, BF>(a, grid, lds, s)
+                 : launch_apply<CPT, kModeDense, false, BF>(a, grid, lds, s);
 }
 
+// bf: the parameters are bfloat16 (ApplyArgs::theta16)
 hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, int64_t grid, size_t lds,
-                          hipStream_t s) {
+                          hipStream_t s, bool bf = false) {
   switch (cpt) {
-    case 1: return launch_apply_cpt<1>(mode, aligned, a, grid, lds, s);
-    case 2: return launch_apply_cpt<2>(mode, aligned, a, grid, lds, s);
-    case 4: return launch_apply_cpt<4>(mode, aligned, a, grid, lds, s);
-    default: return launch_apply_cpt<8>(mode, aligned, a, grid, lds, s);
+    case 1: return bf ? launch_apply_cpt<1, true>(mode, aligned, a, grid, lds, s) : launch_apply_cpt<1, false>(mode, aligned, a, grid, lds, s);
+    case 2: return bf ? launch_apply_cpt<2, true>(mode, aligned, a, grid, lds, s) : launch_apply_cpt<2, false>(mode, aligned, a, grid, lds, s);
+    case 4: return bf ? launch_apply_cpt<4, true>(mode, aligned, a, grid, lds, s) : launch_apply_cpt<4, false>(mode, aligned, a, grid, lds, s);
+    default: return bf ? launch_apply_cpt<8, true>(mode, aligned, a, grid, lds, s) : launch_apply_cpt<8, false>(mode, aligned, a, grid, lds, s);
   }
 }
 
 // The fused step for blocks [0, n_full): the fused kernel, then the blocks it
 // deferred (compress, then update, from the device list).
-template <int CPT, bool EF>
+template <int CPT, bool EF, bool BF>
 hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  hipLaunchKernelGGL((step_full_kernel<CPT, EF>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a, (int64_t)0);
+  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a, (int64_t)0);
   const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
   hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF>), dim3(grid2), dim3(kThreads), 0, s, c);
   ApplyArgs al = a;
   al.blocks = c.deferred;
   al.n_list = c.n_deferred;
-  hipLaunchKernelGGL((apply_list_kernel<CPT>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
+  hipLaunchKernelGGL((apply_list_kernel<CPT, BF>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
   return hipGetLastError();
 }
 
-hipError_t dispatch_fused(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
-                          size_t apply_lds, hipStream_t s) {
+template <bool BF>
+hipError_t dispatch_fused_t(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
+                            size_t apply_lds, hipStream_t s) {
   switch (cpt) {
-    case 1: return ef ? launch_fused<1, true>(c, a, n_full, apply_lds, s) : launch_fused<1, false>(c, a, n_full, apply_lds, s);
-    case 2: return ef ? launch_fused<2, true>(c, a, n_full, apply_lds, s) : launch_fused<2, false>(c, a, n_full, apply_lds, s);
-    default: return ef ? launch_fused<4, true>(c, a, n_full, apply_lds, s) : launch_fused<4, false>(c, a, n_full, apply_lds, s);
+    case 1: return ef ? launch_fused<1, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<1, false, BF>(c, a, n_full, apply_lds, s);
+    case 2: return ef ? launch_fused<2, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<2, false, BF>(c, a, n_full, apply_lds, s);
+    default: return ef ? launch_fused<4, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<4, false, BF>(c, a, n_full, apply_lds, s);
   }
+}
+
+hipError_t dispatch_fused(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
+                          size_t apply_lds, hipStream_t s, bool bf) {
+  return bf ? dispatch_fused_t<true>(cpt, ef, c, a, n_full, apply_lds, s)
+            : dispatch_fused_t<false>(cpt, ef, c, a, n_full, apply_lds, s);
 }
 
 // The global quantizer's launches over all blocks: pass 1 (full aligned
@@ -458,12 +466,15 @@ int ma_set_lr(ma_ctx *h, float lr) {
   return MA_OK;
 }
 
-int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream) {
+namespace {
+
+// One step for fp32 (bf false) or bfloat16 (bf true) parameters.
+int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream_t stream) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_step: null handle");
   if (!params || !grads) return fail(MA_EINVAL, "ma_step: null params or grads");
-  if (((uintptr_t)params & 3u) || ((uintptr_t)grads & 1u))
-    return fail(MA_EINVAL, "ma_step: params must be 4-byte and grads 2-byte aligned");
+  if (((uintptr_t)params & (bf ? 1u : 3u)) || ((uintptr_t)grads & 1u))
+    return fail(MA_EINVAL, "ma_step: params must be element-aligned and grads 2-byte aligned");
   DeviceGuard guard(h->device);
   if (!guard.ok) return fail(MA_EHIP, "ma_step: cannot select device %d", h->device);
 
@@ -490,7 +501,8 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   ca.n_deferred = h->n_deferred;
 
   ApplyArgs aa = make_apply_args(h, t, c1, c2, decay);
-  aa.theta = params;
+  aa.theta = bf ? nullptr : static_cast<float *>(params);
+  aa.theta16 = bf ? static_cast<uint16_t *>(params) : nullptr;
   aa.touched = h->count_touched ? h->touched : nullptr;
 
   const bool b8 = (h->B % 8) == 0;
@@ -531,7 +543,7 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     e = dispatch_global_q(h->cpt, g_al, ca, h->n_b, n_full, stream);
     if (t1) (void)hipEventRecord(t1, stream);
     if (t2) (void)hipEventRecord(t2, stream);
-    if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream);
+    if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream, bf);
     if (t3) {
       (void)hipEventRecord(t3, stream);
       h->events.push_back({0, t0, t1});
@@ -555,7 +567,7 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h))))
       return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     if (t0) (void)hipEventRecord(t0, stream);
-    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, ca, aa, n_full, h->apply_lds, stream);
+    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, ca, aa, n_full, h->apply_lds, stream, bf);
     if (t1) {
       (void)hipEventRecord(t1, stream);
       h->events.push_back({2, t0, t1});
@@ -564,7 +576,7 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
       e = dispatch_compress(h->cpt, g_al, ef, ca, n_full, h->n_b, n_full, stream);
       ApplyArgs at = aa;
       at.first_block = n_full;
-      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, h->apply_lds, stream);
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, h->apply_lds, stream, bf);
     }
     if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
     h->t = t;
@@ -611,7 +623,7 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
     if (h->timing && !(u0 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     if (h->timing && !(u1 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     if (u0) (void)hipEventRecord(u0, upd);
-    e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, h->apply_lds, upd);
+    e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, h->apply_lds, upd, bf);
     if (u1) {
       (void)hipEventRecord(u1, upd);
       h->events.push_back({1, u0, u1});
@@ -627,6 +639,16 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
   h->last_c1 = c1;
   h->last_c2 = c2;
   return MA_OK;
+}
+
+}  // namespace
+
+int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream) {
+  return step_impl(h, params, false, grads, stream);
+}
+
+int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream) {
+  return step_impl(h, params, true, grads, stream);
 }
 
 int ma_read_state(const ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, void *host_dst) {

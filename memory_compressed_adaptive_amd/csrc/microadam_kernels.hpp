@@ -869,7 +869,8 @@ __global__ __launch_bounds__(kThreads) void global_minmax_kernel(const float *bl
 // ------------------------------------------------------------------ adamstats_apply
 
 struct ApplyArgs {
-  float *theta;             // parameters [d] (MODE 0, 1)
+  float *theta;             // fp32 parameters [d] (MODE 0, 1)
+  uint16_t *theta16;        // or bfloat16 parameters [d] (the BF variants)
   const uint32_t *G;        // window [m][k]
   const int64_t *off_tab;   // [n_b + 1]
   const float *betapow;     // [2m]: beta1^r, then beta2^r, r = 0..m-1
@@ -885,6 +886,21 @@ struct ApplyArgs {
 };
 
 enum { kModeSparse = 0, kModeDense = 1, kModeMoments = 2 };
+
+// Parameter access for fp32 (BF false) or bfloat16 (BF true) parameters.  A
+// bfloat16 parameter is widened exactly, updated in fp32 like an fp32 one, and
+// the result rounded to nearest even once.
+template <bool BF>
+__device__ __forceinline__ float ld_param(const ApplyArgs &A, int64_t i) {
+  return BF ? bf16_bits_to_f32(A.theta16[i]) : A.theta[i];
+}
+template <bool BF>
+__device__ __forceinline__ void st_param(const ApplyArgs &A, int64_t i, float v) {
+  if (BF)
+    A.theta16[i] = (uint16_t)f32_to_bf16_rne(v);
+  else
+    A.theta[i] = v;
+}
 constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
 constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over
 
@@ -908,7 +924,7 @@ struct ApplySmem {
 // MODE 2: write m_hat and v_hat of the block to row out_row of the outputs;
 //         parameters untouched.
 // PRELOADED: the block's window entries are already in sm.ent.
-template <int CPT, int MODE, bool ALIGNED, bool PRELOADED>
+template <int CPT, int MODE, bool ALIGNED, bool PRELOADED, bool BF = false>
 __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64_t out_row, const ApplySmem &sm) {
   constexpr int W = CPT * kChunkSpan / 32;          // bitmap words
   constexpr int WPT = (W + kThreads - 1) / kThreads;
@@ -1024,7 +1040,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
 #pragma unroll
       for (int u = 0; u < kThetaPerThread; ++u) {
         const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
-        thv[u] = (x < n) ? A.theta[s + s_pos[x]] : 0.f;
+        thv[u] = (x < n) ? ld_param<BF>(A, s + s_pos[x]) : 0.f;
       }
     }
     // dense: the thread's 8 consecutive parameters of each chunk, streamed
@@ -1039,14 +1055,20 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         tb[c] = (i0 < L) ? (s_bits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
         tb[c] |= tb[c] ? 0x100u : 0u;   // bit 8: the thread's 8 parameters are streamed
         if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
-          if (ALIGNED && i0 + kChunk <= L) {
+          if (ALIGNED && BF && i0 + kChunk <= L) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(A.theta16 + s + i0);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < kChunk; ++e)
+              th[c][e] = (e & 1) ? u2f(ww[e >> 1] & 0xffff0000u) : u2f(ww[e >> 1] << 16);
+          } else if (ALIGNED && i0 + kChunk <= L) {
             const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
             const float4 v1 = *reinterpret_cast<const float4 *>(A.theta + s + i0 + 4);
             th[c][0] = v0.x; th[c][1] = v0.y; th[c][2] = v0.z; th[c][3] = v0.w;
             th[c][4] = v1.x; th[c][5] = v1.y; th[c][6] = v1.z; th[c][7] = v1.w;
           } else {
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? A.theta[s + i0 + e] : 0.f;
+            for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? ld_param<BF>(A, s + i0 + e) : 0.f;
           }
         } else {
 #pragma unroll
@@ -1116,7 +1138,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         if (x < n) {
           const float mh = A.c1 * s_z1[x];
           const float vh = A.c2 * s_z2[x];
-          A.theta[s + s_pos[x]] = thv[u] - A.lr * (mh / (sqrtf(vh) + A.eps));
+          st_param<BF>(A, s + s_pos[x], thv[u] - A.lr * (mh / (sqrtf(vh) + A.eps)));
         }
       }
     } else if (MODE == kModeDense) {
@@ -1139,13 +1161,20 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
               }
             }
           }
-          if (ALIGNED && i0 + kChunk <= L) {
+          if (ALIGNED && BF && i0 + kChunk <= L) {
+            u32x4 w;
+            w.x = f32_to_bf16_rne(th[c][0]) | (f32_to_bf16_rne(th[c][1]) << 16);
+            w.y = f32_to_bf16_rne(th[c][2]) | (f32_to_bf16_rne(th[c][3]) << 16);
+            w.z = f32_to_bf16_rne(th[c][4]) | (f32_to_bf16_rne(th[c][5]) << 16);
+            w.w = f32_to_bf16_rne(th[c][6]) | (f32_to_bf16_rne(th[c][7]) << 16);
+            *reinterpret_cast<u32x4 *>(A.theta16 + s + i0) = w;
+          } else if (ALIGNED && i0 + kChunk <= L) {
             *reinterpret_cast<float4 *>(A.theta + s + i0) = make_float4(th[c][0], th[c][1], th[c][2], th[c][3]);
             *reinterpret_cast<float4 *>(A.theta + s + i0 + 4) = make_float4(th[c][4], th[c][5], th[c][6], th[c][7]);
           } else {
 #pragma unroll
             for (int e = 0; e < kChunk; ++e)
-              if (i0 + e < L) A.theta[s + i0 + e] = th[c][e];
+              if (i0 + e < L) st_param<BF>(A, s + i0 + e, th[c][e]);
           }
         }
       }
@@ -1176,7 +1205,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       const int i0 = c * kChunkSpan + tid * kChunk;
 #pragma unroll
       for (int e = 0; e < kChunk; ++e)
-        if (i0 + e < L) A.theta[s + i0 + e] = A.theta[s + i0 + e] * A.decay;
+        if (i0 + e < L) st_param<BF>(A, s + i0 + e, ld_param<BF>(A, s + i0 + e) * A.decay);
     }
   }
 }
@@ -1201,24 +1230,24 @@ __device__ __forceinline__ ApplySmem apply_smem(const ApplyArgs &A, uint32_t *sm
 
 // One workgroup per block: blocks first_block .. first_block + grid - 1
 // (MODE 0, 1) or the listed blocks (MODE 2).
-template <int CPT, int MODE, bool ALIGNED>
+template <int CPT, int MODE, bool ALIGNED, bool BF = false>
 __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t s_cnt[kWaves + 1];
   const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x]
                                            : A.first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
-  apply_block<CPT, MODE, ALIGNED, false>(A, j, (int64_t)blockIdx.x, apply_smem<CPT>(A, smem, s_cnt, j));
+  apply_block<CPT, MODE, ALIGNED, false, BF>(A, j, (int64_t)blockIdx.x, apply_smem<CPT>(A, smem, s_cnt, j));
 }
 
 // The sparse update of the blocks in the device list A.blocks[0 .. *A.n_list).
-template <int CPT>
+template <int CPT, bool BF = false>
 __global__ __launch_bounds__(kThreads) void apply_list_kernel(ApplyArgs A) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t s_cnt[kWaves + 1];
   const unsigned int n = *A.n_list;
   for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
     const int64_t j = A.blocks[q];
-    apply_block<CPT, kModeSparse, false, false>(A, j, 0, apply_smem<CPT>(A, smem, s_cnt, j));
+    apply_block<CPT, kModeSparse, false, false, BF>(A, j, 0, apply_smem<CPT>(A, smem, s_cnt, j));
     __syncthreads();
   }
 }
@@ -1238,7 +1267,7 @@ constexpr int kFusedEnt = 1984;
 // phases, so the VALU-bound compressor and the memory-bound update share each
 // CU.  A block the compressor defers is left entirely (compress and update)
 // to compress_deferred_kernel and apply_list_kernel.
-template <int CPT, bool EF>
+template <int CPT, bool EF, bool BF = false>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(CompressArgs C, ApplyArgs A,
                                                                              int64_t first_block) {
   __shared__ CompressSmem<CPT> sm;
@@ -1292,7 +1321,7 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   as.cnt = sm.cnt;
   as.ent_stride = es;
   as.in_lds = true;
-  apply_block<CPT, kModeSparse, false, true>(A, j, 0, as);
+  apply_block<CPT, kModeSparse, false, true, BF>(A, j, 0, as);
 }
 
 }  // namespace microadam

@@ -60,12 +60,15 @@ class MicroAdam:
 
     # ------------------------------------------------------------ the step
     def step(self, params, grads, stream=None):
+        """params: fp32 (4-byte elements) or bfloat16 (2-byte elements, updated
+        through ma_step_bf16)."""
         assert params.is_cuda and grads.is_cuda
         assert params.numel() == self.d and grads.numel() == self.d
         assert params.is_contiguous() and grads.is_contiguous()
-        assert params.element_size() == 4 and grads.element_size() == 2
-        _L.check(_L.lib().ma_step(self._h, C.c_void_p(params.data_ptr()), C.c_void_p(grads.data_ptr()),
-                                  C.c_void_p(_stream_handle(stream))))
+        assert params.element_size() in (2, 4) and grads.element_size() == 2
+        fn = _L.lib().ma_step if params.element_size() == 4 else _L.lib().ma_step_bf16
+        _L.check(fn(self._h, C.c_void_p(params.data_ptr()), C.c_void_p(grads.data_ptr()),
+                    C.c_void_p(_stream_handle(stream))))
 
     # ------------------------------------------------------------ accessors
     @property

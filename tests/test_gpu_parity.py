@@ -169,6 +169,43 @@ def test_global_quantizer_single_block_equals_block_mode():
         assert_bits_equal("block vs global, one block", a, b)
 
 
+@pytest.mark.parametrize("d,B,k,m,wd,flags,misalign", [
+    (100_003, 16384, 1000, 4, 0.0, 0, False),                  # fused kernel + ragged block
+    (100_003, 16384, 1000, 4, 0.0, L.MA_FLAG_UNFUSED, False),  # sparse two-kernel update
+    (70_000, 16384, 700, 4, 0.1, 0, False),                    # decay: dense update, 16-byte rows
+    (70_000, 16384, 700, 4, 0.1, 0, True),                     # decay, parameters 2 bytes off
+    (20_011, 1003, 500, 3, 0.0, 0, False),                     # odd B_d
+])
+def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
+    # ma_step_bf16: widen, fp32 step, round to nearest even once
+    rng = np.random.default_rng(8)
+    lr = 1e-2 if wd else 1e-3
+    th16 = O.bf16_rne((rng.standard_normal(d) * 0.02).astype(np.float32))
+    opt = MicroAdam(d, B, k, m, lr=lr, wd=wd)
+    opt.set_flags(flags)
+    orc = O.FullState(O.make_cfg(d, B, k, m, 4, 0.9, 0.999, 1e-8, lr, wd, 42, 0))
+    th_cpu = th16.copy()
+    if misalign:
+        buf = torch.empty(d + 1, dtype=torch.int16, device="cuda")
+        th_gpu = buf[1:]
+    else:
+        th_gpu = torch.empty(d, dtype=torch.int16, device="cuda")
+    th_gpu.copy_(torch.from_numpy(th16.view(np.int16)))
+    changed = 0
+    for t in range(1, 6):
+        g = gauss_grads(rng, d, t)
+        say(f"[bf16 params] step {t}: d={d} B={B} m={m} wd={wd} flags={flags} misalign={misalign}")
+        opt.step(th_gpu, to_gpu_bf16(g))
+        torch.cuda.synchronize()
+        before = th_cpu.copy()
+        orc.step_bf16(th_cpu, g)
+        changed += int((before != th_cpu).sum())
+        assert_bits_equal(f"bf16 t={t} window", opt.window(), orc.G)
+        assert_bits_equal(f"bf16 t={t} codes", opt.codes_bytes(), orc.ef)
+        assert_bits_equal(f"bf16 t={t} theta", th_gpu.cpu().numpy().view(np.uint16), th_cpu)
+    assert changed > 0
+
+
 def test_long_window_multi_pass_slots():
     # m * k_b > LDS slots: the update kernel runs several slot passes
     full_parity("m=37 k=d/10", 40_000, 16384, 4_000, 37, 40, moments=True)
