@@ -71,6 +71,8 @@ def main():
     ap.add_argument("--bf16-params", action="store_true",
                     help="bfloat16 parameters (ma_step_bf16): the one-40-GB-GPU regime")
     ap.add_argument("--wd", type=float, default=0.0, help="decoupled weight decay (dense update)")
+    ap.add_argument("--optimizer", choices=("microadam", "adamw"), default="microadam",
+                    help="adamw: the page's fp32 AdamW comparison point on the same harness")
     ap.add_argument("--global-quant", action="store_true",
                     help="one (delta, Delta) over all d (two compressor passes); no oracle leg")
     ap.add_argument("--chunks", type=int, default=0,
@@ -115,6 +117,10 @@ def main():
     del src, dst
     torch.cuda.empty_cache()
     log(f"copy kernel: {copy_gbps:.0f} GB/s")
+
+    if args.optimizer == "adamw":
+        bench_adamw(args, w, K, W, copy_gbps, dev)
+        return
 
     # ---------------- inputs resident in HBM
     theta = torch.empty(d, dtype=torch.float32, device=dev)
@@ -323,6 +329,78 @@ def main():
         log(f"cpu baseline {cpu_steps_per_s:.5f} steps/s (extrapolated); parity ok={result['parity_sampled']['ok']}")
 
     opt.close()
+    print(json.dumps(result), flush=True)
+
+
+def bench_adamw(args, w, K, W, copy_gbps, dev):
+    """The fp32 AdamW baseline (ma_adamw_step) on the same parameters and
+    gradients: 8 bytes of state per parameter, 26 bytes moved per parameter."""
+    import numpy as np
+    import torch
+
+    from memory_compressed_adaptive_amd import synth
+    from memory_compressed_adaptive_amd.baselines import adamw_step
+
+    d = w.d
+    theta = torch.empty(d, dtype=torch.float32, device=dev)
+    synth.fill_params(theta)
+    m = torch.zeros(d, dtype=torch.float32, device=dev)
+    v = torch.zeros_like(m)
+    gsrc = synth.GradSource(w)
+    free, _ = torch.cuda.mem_get_info()
+    P = max(1, min(K + W, int((free - (8 << 30)) // (2 * d))))
+    pool = []
+    for p in range(P):
+        g = torch.empty(d, dtype=torch.int16, device=dev)
+        gsrc.fill(g, p + 1)
+        pool.append(g)
+    # oracle sample: a contiguous run (AdamW is elementwise)
+    n_s = min(d, 1 << 21) if not args.no_cpu_baseline else 0
+    th_s = theta[:n_s].cpu().numpy().copy() if n_s else None
+    g_s = [g[:n_s].cpu().numpy().view(np.uint16) for g in pool] if n_s else None
+    torch.cuda.synchronize()
+    for s in range(W):
+        adamw_step(theta, pool[s % P], m, v, s + 1, lr=1e-4, wd=args.wd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for s in range(W, W + K):
+        adamw_step(theta, pool[s % P], m, v, s + 1, lr=1e-4, wd=args.wd)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_launch = e0.elapsed_time(e1) / K
+    steps_per_s = K / elapsed
+    bytes_step = 26 * d
+    achieved = bytes_step / (ms_launch * 1e-3) / 1e9
+    result = {
+        "metric": METRIC + " (comparison: fp32 AdamW)", "value": round(steps_per_s, 3), "unit": "steps/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "d": d, "optimizer": "adamw fp32", "wd": args.wd, "grad_pool": P},
+        "params_per_s": round(d * steps_per_s, 1), "state_bytes": 8 * d,
+        "roofline": {"bound": "hbm", "kernel": "adamw", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": bytes_step, "avg_launch_ms": round(ms_launch, 4), "launches_per_step": 1},
+        "hbm": {"copy_kernel_GBps": round(copy_gbps, 1)},
+    }
+    if n_s:
+        import oracle as O
+        mo = np.zeros(n_s, np.float32)
+        vo = np.zeros(n_s, np.float32)
+        c0 = time.perf_counter()
+        for s in range(W + K):
+            O.adamw_step(s + 1, th_s, g_s[s % P], mo, vo, lr=1e-4, wd=args.wd)
+        c1 = time.perf_counter()
+        got = theta[:n_s].cpu().numpy()
+        result["cpu_baseline"] = {
+            "value": round(1.0 / ((c1 - c0) / (W + K) * d / n_s), 6), "unit": "steps/s", "cores": 1,
+            "kind": "oracle", "host_cpus": os.cpu_count(),
+            "sample": f"the first {n_s} of {d} parameters x {W + K} steps, {c1 - c0:.1f} s single-threaded, "
+                      f"extrapolated to all parameters"}
+        result["parity_sampled"] = {"elements": n_s, "steps": W + K,
+                                    "ok": bool(np.array_equal(got.view(np.uint32), th_s.view(np.uint32)))}
     print(json.dumps(result), flush=True)
 
 

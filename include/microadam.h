@@ -107,6 +107,20 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
  */
 int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream);
 
+/*
+ * Comparison baseline: one fp32 AdamW step (the 8d-byte optimizer the second
+ * paragraph compares against), stateless, on caller-owned device arrays of n
+ * elements: theta, m, v fp32 (updated in place), grads bf16 (raw bits).  Step t
+ * is 1-based; with m = v = 0 before step 1.  Per element, each operation
+ * rounded once in fp32: m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g*g;
+ * theta = theta*decay - lr*((m*r1)/(sqrtf(v*r2) + eps)), where (1-b),
+ * decay = 1 - lr*wd and r = 1/(1 - b^t) are computed in double and rounded to
+ * fp32.  Enqueued on `stream`.  MA_EINVAL for n < 0, t < 1, a null or
+ * misaligned pointer (4 bytes for fp32, 2 for bf16); MA_OK for n = 0.
+ */
+int ma_adamw_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
+                  const uint16_t *grads, float *m, float *v, hipStream_t stream);
+
 /* Optimizer-state bytes the second paragraph of the MicroAdam page counts:
  * ceil(d/2) + 4*m*k (0.9d at m = 10, k = d/100).  0 for NULL. */
 size_t ma_state_bytes(const ma_ctx *h);

@@ -12,6 +12,7 @@
 
 #include "microadam.h"
 #include "microadam_kernels.hpp"
+#include "adamw_kernels.hpp"
 
 using namespace microadam;
 
@@ -649,6 +650,41 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
 
 int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream) {
   return step_impl(h, params, true, grads, stream);
+}
+
+int ma_adamw_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
+                  const uint16_t *grads, float *m, float *v, hipStream_t stream) {
+  clear_error();
+  if (n < 0 || t < 1) return fail(MA_EINVAL, "ma_adamw_step: n must be >= 0 and t >= 1");
+  if (n == 0) return MA_OK;
+  if (!theta || !grads || !m || !v) return fail(MA_EINVAL, "ma_adamw_step: null pointer");
+  if (((uintptr_t)theta & 3u) || ((uintptr_t)m & 3u) || ((uintptr_t)v & 3u) || ((uintptr_t)grads & 1u))
+    return fail(MA_EINVAL, "ma_adamw_step: misaligned pointer");
+  AdamwArgs a;
+  a.theta = theta;
+  a.g = grads;
+  a.m = m;
+  a.v = v;
+  a.n = n;
+  a.b1 = beta1;
+  a.b2 = beta2;
+  a.omb1 = (float)(1.0 - (double)beta1);
+  a.omb2 = (float)(1.0 - (double)beta2);
+  a.r1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)t)));
+  a.r2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)t)));
+  a.decay = (float)(1.0 - (double)lr * (double)wd);
+  a.lr = lr;
+  a.eps = eps;
+  const bool al = (((uintptr_t)theta | (uintptr_t)m | (uintptr_t)v | (uintptr_t)grads) & 15u) == 0;
+  const int64_t runs = (n + 7) / 8;
+  const unsigned grid = (unsigned)std::min<int64_t>((runs + kAdamwThreads - 1) / kAdamwThreads, 256 * 16);
+  if (al)
+    hipLaunchKernelGGL(adamw_kernel<true>, dim3(grid), dim3(kAdamwThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(adamw_kernel<false>, dim3(grid), dim3(kAdamwThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MA_EHIP, "ma_adamw_step: launch failed: %s", hipGetErrorString(e));
+  return MA_OK;
 }
 
 int ma_read_state(const ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, void *host_dst) {

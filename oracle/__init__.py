@@ -68,6 +68,8 @@ def lib():
     L.orc_dequant_group.argtypes = [p, i64, f32, f32, p]
     L.orc_block_step.restype = C.c_int
     L.orc_block_step.argtypes = [cfgp, i64, i64, p, p, p, i64, p, p, i64, p, p]
+    L.orc_adamw_step.restype = None
+    L.orc_adamw_step.argtypes = [i64, i64, C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, p, p, p, p]
     L.orc_step.restype = C.c_int
     L.orc_step.argtypes = [cfgp, i64, p, p, p, p, p, p, p]
     L.orc_state_bytes.restype = u64
@@ -288,3 +290,11 @@ class BlockState:
             raise ValueError(f"oracle rejected the configuration (rc={rc})")
         self.t += 1
         return (mh, vh) if moments else None
+
+
+def adamw_step(t, theta, g_bf16, m, v, beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-4, wd=0.0):
+    """The fp32 AdamW baseline (orc_adamw_step), in place on theta, m, v."""
+    g = np.ascontiguousarray(g_bf16, dtype=np.uint16)
+    for a in (theta, m, v):
+        assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == g.size
+    lib().orc_adamw_step(g.size, int(t), beta1, beta2, eps, lr, wd, _ptr(theta), _ptr(g), _ptr(m), _ptr(v))

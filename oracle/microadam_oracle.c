@@ -439,6 +439,26 @@ int orc_step(const orc_cfg *c, int64_t t, float *theta, const uint16_t *g,
     return 0;
 }
 
+/* The baseline AdamW of the comparison in the second paragraph (fp32 m and v,
+ * 8 bytes of state per parameter), in the decoupled-decay form used above. */
+void orc_adamw_step(int64_t n, int64_t t, float b1, float b2, float eps, float lr, float wd,
+                    float *theta, const uint16_t *g, float *m, float *v)
+{
+    const float omb1 = (float)(1.0 - (double)b1);
+    const float omb2 = (float)(1.0 - (double)b2);
+    const float r1 = (float)(1.0 / (1.0 - pow((double)b1, (double)t)));
+    const float r2 = (float)(1.0 / (1.0 - pow((double)b2, (double)t)));
+    const float decay = (float)(1.0 - (double)lr * (double)wd);
+    for (int64_t i = 0; i < n; ++i) {
+        float gi = orc_bf16_to_f32(g[i]);
+        m[i] = b1 * m[i] + omb1 * gi;
+        v[i] = b2 * v[i] + omb2 * (gi * gi);
+        float mh = m[i] * r1;
+        float vh = v[i] * r2;
+        theta[i] = theta[i] * decay - lr * (mh / (sqrtf(vh) + eps));
+    }
+}
+
 uint64_t orc_state_bytes(const orc_cfg *c)
 {
     return (uint64_t)((c->d + 1) / 2) + 4ull * (uint64_t)c->m * (uint64_t)c->k;

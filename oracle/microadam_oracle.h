@@ -94,6 +94,16 @@ int orc_block_step(const orc_cfg *c, int64_t t, int64_t j,
 int orc_step(const orc_cfg *c, int64_t t, float *theta, const uint16_t *g,
              uint8_t *ef, float *stats, uint32_t *G, float *mhat, float *vhat);
 
+/* ---- comparison baseline: fp32 AdamW (the second paragraph's 8d-byte
+ * optimizer), one step t (1-based) over n elements, in place.  Per element,
+ * each operation rounded once in fp32:
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *   theta = theta*decay - lr*((m*r1) / (sqrtf(v*r2) + eps))
+ * with g the bf16 gradient widened, (1-b), decay = 1 - lr*wd and the bias
+ * factors r = 1/(1 - b^t) computed in double and rounded to fp32. */
+void orc_adamw_step(int64_t n, int64_t t, float b1, float b2, float eps, float lr, float wd,
+                    float *theta, const uint16_t *g, float *m, float *v);
+
 /* array helpers */
 void orc_bf16_rne_array(const float *x, int64_t n, uint16_t *out);
 void orc_pcg_hash_array(const uint32_t *x, int64_t n, uint32_t *out);

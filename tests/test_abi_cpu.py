@@ -69,3 +69,11 @@ def test_null_handles_are_safe():
     assert lib.ma_kernel_times(None, None, None, 0) == L.MA_EINVAL
     assert lib.ma_set_pipeline(None, 4) == L.MA_EINVAL
     assert lib.ma_get_pipeline(None) == -1
+
+
+def test_adamw_argument_checks_without_gpu():
+    lib = L.lib()
+    assert lib.ma_adamw_step(-1, 1, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_EINVAL
+    assert lib.ma_adamw_step(10, 0, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_EINVAL
+    assert lib.ma_adamw_step(0, 1, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_OK
+    assert lib.ma_adamw_step(10, 1, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_EINVAL

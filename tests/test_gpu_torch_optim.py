@@ -111,6 +111,6 @@ def test_reduces_a_synthetic_regression_loss():
         loss = torch.nn.functional.mse_loss(model(X), y)
         loss.backward()
         opt.step()
-        losses.append(float(loss))
+        losses.append(float(loss.detach()))
     say(f"[torch optim] loss {losses[0]:.4f} -> {losses[-1]:.4f}")
     assert losses[-1] < 0.5 * losses[0]
