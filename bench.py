@@ -71,8 +71,8 @@ def main():
     ap.add_argument("--bf16-params", action="store_true",
                     help="bfloat16 parameters (ma_step_bf16): the one-40-GB-GPU regime")
     ap.add_argument("--wd", type=float, default=0.0, help="decoupled weight decay (dense update)")
-    ap.add_argument("--optimizer", choices=("microadam", "adamw"), default="microadam",
-                    help="adamw: the page's fp32 AdamW comparison point on the same harness")
+    ap.add_argument("--optimizer", choices=("microadam", "adamw", "adamw8"), default="microadam",
+                    help="adamw / adamw8: the page's fp32 and 8-bit AdamW comparison points, same harness")
     ap.add_argument("--global-quant", action="store_true",
                     help="one (delta, Delta) over all d (two compressor passes); no oracle leg")
     ap.add_argument("--chunks", type=int, default=0,
@@ -118,7 +118,7 @@ def main():
     torch.cuda.empty_cache()
     log(f"copy kernel: {copy_gbps:.0f} GB/s")
 
-    if args.optimizer == "adamw":
+    if args.optimizer in ("adamw", "adamw8"):
         bench_adamw(args, w, K, W, copy_gbps, dev)
         return
 
@@ -339,13 +339,25 @@ def bench_adamw(args, w, K, W, copy_gbps, dev):
     import torch
 
     from memory_compressed_adaptive_amd import synth
-    from memory_compressed_adaptive_amd.baselines import adamw_step
+    from memory_compressed_adaptive_amd.baselines import Q8_BLOCK, adamw8_step, adamw_step
 
     d = w.d
+    q8 = args.optimizer == "adamw8"
     theta = torch.empty(d, dtype=torch.float32, device=dev)
     synth.fill_params(theta)
-    m = torch.zeros(d, dtype=torch.float32, device=dev)
-    v = torch.zeros_like(m)
+    if q8:
+        nq = -(-d // Q8_BLOCK)
+        st = (torch.zeros(d, dtype=torch.int8, device=dev), torch.zeros(d, dtype=torch.uint8, device=dev),
+              torch.zeros(nq, dtype=torch.float32, device=dev), torch.zeros(nq, dtype=torch.float32, device=dev))
+
+        def one(g, t):
+            adamw8_step(theta, g, *st, t, lr=1e-4, wd=args.wd)
+    else:
+        m = torch.zeros(d, dtype=torch.float32, device=dev)
+        v = torch.zeros_like(m)
+
+        def one(g, t):
+            adamw_step(theta, g, m, v, t, lr=1e-4, wd=args.wd)
     gsrc = synth.GradSource(w)
     free, _ = torch.cuda.mem_get_info()
     P = max(1, min(K + W, int((free - (8 << 30)) // (2 * d))))
@@ -360,27 +372,31 @@ def bench_adamw(args, w, K, W, copy_gbps, dev):
     g_s = [g[:n_s].cpu().numpy().view(np.uint16) for g in pool] if n_s else None
     torch.cuda.synchronize()
     for s in range(W):
-        adamw_step(theta, pool[s % P], m, v, s + 1, lr=1e-4, wd=args.wd)
+        one(pool[s % P], s + 1)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for s in range(W, W + K):
-        adamw_step(theta, pool[s % P], m, v, s + 1, lr=1e-4, wd=args.wd)
+        one(pool[s % P], s + 1)
     e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_launch = e0.elapsed_time(e1) / K
     steps_per_s = K / elapsed
-    bytes_step = 26 * d
+    # parameter r+w, gradient, moments r+w (fp32: 4 B each; 8-bit: 1 B each + scales)
+    bytes_step = (8 + 2 + 4 + 16 * (-(-d // Q8_BLOCK)) / d) * d if q8 else 26 * d
+    bytes_step = int(bytes_step)
     achieved = bytes_step / (ms_launch * 1e-3) / 1e9
     result = {
-        "metric": METRIC + " (comparison: fp32 AdamW)", "value": round(steps_per_s, 3), "unit": "steps/s",
+        "metric": METRIC + (" (comparison: 8-bit AdamW)" if q8 else " (comparison: fp32 AdamW)"), "value": round(steps_per_s, 3), "unit": "steps/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(elapsed * 1e3 / K, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": w.name, "d": d, "optimizer": "adamw fp32", "wd": args.wd, "grad_pool": P},
-        "params_per_s": round(d * steps_per_s, 1), "state_bytes": 8 * d,
-        "roofline": {"bound": "hbm", "kernel": "adamw", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+        "config": {"workload": w.name, "d": d, "optimizer": "adamw 8-bit" if q8 else "adamw fp32", "wd": args.wd,
+                   "grad_pool": P},
+        "params_per_s": round(d * steps_per_s, 1),
+        "state_bytes": 2 * d + 8 * (-(-d // Q8_BLOCK)) if q8 else 8 * d,
+        "roofline": {"bound": "hbm", "kernel": "adamw8" if q8 else "adamw", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": bytes_step, "avg_launch_ms": round(ms_launch, 4), "launches_per_step": 1},
         "hbm": {"copy_kernel_GBps": round(copy_gbps, 1)},
@@ -389,9 +405,15 @@ def bench_adamw(args, w, K, W, copy_gbps, dev):
         import oracle as O
         mo = np.zeros(n_s, np.float32)
         vo = np.zeros(n_s, np.float32)
+        ns_q = -(-n_s // Q8_BLOCK)
+        q8s = (np.zeros(n_s, np.int8), np.zeros(n_s, np.uint8), np.zeros(ns_q, np.float32),
+               np.zeros(ns_q, np.float32))
         c0 = time.perf_counter()
         for s in range(W + K):
-            O.adamw_step(s + 1, th_s, g_s[s % P], mo, vo, lr=1e-4, wd=args.wd)
+            if q8:
+                O.adamw8_step(s + 1, th_s, g_s[s % P], *q8s, lr=1e-4, wd=args.wd)
+            else:
+                O.adamw_step(s + 1, th_s, g_s[s % P], mo, vo, lr=1e-4, wd=args.wd)
         c1 = time.perf_counter()
         got = theta[:n_s].cpu().numpy()
         result["cpu_baseline"] = {

@@ -121,6 +121,21 @@ int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t
 int ma_adamw_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
                   const uint16_t *grads, float *m, float *v, hipStream_t stream);
 
+/*
+ * Comparison baseline: one 8-bit block-quantized AdamW step (the 2d-byte
+ * optimizer the second paragraph compares against).  The page fixes no 8-bit
+ * scheme; this one: blocks of 256 elements, each with scales sm = max|m| and
+ * sr = max sqrt(v); cm: int8 codes rint(m * (127/sm)); cv: uint8 codes
+ * rint(sqrt(v) * (255/sr)) (round to nearest even; a zero block has scale 0
+ * and codes 0).  A step dequantizes m~ = cm * (sm/127), v~ = (cv * (sr/255))^2,
+ * applies the ma_adamw_step recurrence and update to them, and requantizes the
+ * new moments with the block's new scales.  Arrays caller-owned on the device:
+ * theta fp32[n], grads bf16[n], cm int8[n], cv uint8[n], sm, sr fp32[ceil(n/256)]
+ * (all zero before step 1).  Errors as ma_adamw_step.
+ */
+int ma_adamw8_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
+                   const uint16_t *grads, int8_t *cm, uint8_t *cv, float *sm, float *sr, hipStream_t stream);
+
 /* Optimizer-state bytes the second paragraph of the MicroAdam page counts:
  * ceil(d/2) + 4*m*k (0.9d at m = 10, k = d/100).  0 for NULL. */
 size_t ma_state_bytes(const ma_ctx *h);

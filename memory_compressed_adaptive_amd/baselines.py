@@ -1,6 +1,7 @@
-"""The page's comparison optimizer on the same device path: fp32 AdamW (8 bytes
-of state per parameter, second paragraph of the MicroAdam page), one step per
-call of ma_adamw_step in libmicroadam."""
+"""The page's comparison optimizers on the same device path (second paragraph
+of the MicroAdam page): fp32 AdamW (8 bytes of state per parameter, one call
+of ma_adamw_step) and 8-bit block-quantized AdamW (2 bytes plus 8 per 256
+parameters, ma_adamw8_step)."""
 from __future__ import annotations
 
 import ctypes as C
@@ -20,3 +21,24 @@ def adamw_step(theta, grads, m, v, t: int, beta1=0.9, beta2=0.999, eps=1e-8, lr=
     _L.check(_L.lib().ma_adamw_step(n, int(t), beta1, beta2, eps, lr, wd, C.c_void_p(theta.data_ptr()),
                                     C.c_void_p(grads.data_ptr()), C.c_void_p(m.data_ptr()),
                                     C.c_void_p(v.data_ptr()), C.c_void_p(int(s.cuda_stream))))
+
+
+Q8_BLOCK = 256
+
+
+def adamw8_step(theta, grads, cm, cv, sm, sr, t: int, beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-4, wd=0.0,
+                stream=None):
+    """theta fp32, grads bf16/int16, cm int8, cv uint8 (n elements each), sm and
+    sr fp32 (ceil(n/256) each), all contiguous CUDA tensors; t >= 1."""
+    import torch
+    n = theta.numel()
+    nq = -(-n // Q8_BLOCK)
+    assert theta.is_cuda and theta.is_contiguous() and theta.element_size() == 4
+    assert grads.numel() == n and grads.element_size() == 2 and grads.is_contiguous()
+    assert cm.numel() == n and cv.numel() == n and cm.element_size() == 1 and cv.element_size() == 1
+    assert sm.numel() == nq and sr.numel() == nq and sm.element_size() == 4 and sr.element_size() == 4
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _L.check(_L.lib().ma_adamw8_step(n, int(t), beta1, beta2, eps, lr, wd, C.c_void_p(theta.data_ptr()),
+                                     C.c_void_p(grads.data_ptr()), C.c_void_p(cm.data_ptr()),
+                                     C.c_void_p(cv.data_ptr()), C.c_void_p(sm.data_ptr()),
+                                     C.c_void_p(sr.data_ptr()), C.c_void_p(int(s.cuda_stream))))

@@ -68,3 +68,117 @@ __global__ __launch_bounds__(kAdamwThreads) void adamw_kernel(AdamwArgs A) {
 }
 
 }  // namespace microadam
+
+namespace microadam {
+
+// ------------------------------------------------------------------ 8-bit AdamW
+// The page's other comparison point (2 bytes of state per parameter).  The
+// page fixes no 8-bit scheme; this one: blocks of 256 elements with two fp32
+// scales; m as int8 codes of m * (127 / max|m|), v as uint8 codes of
+// sqrt(v) * (255 / max sqrt(v)), both rounded to nearest even.  A step
+// dequantizes, applies the AdamW recurrence and update above, and requantizes
+// the new moments with the block's new scales.  One wave per block, 4
+// consecutive elements per lane; the block maxima are wave reductions.
+
+constexpr int kQ8Block = 256;
+
+struct Adamw8Args {
+  float *theta;
+  const uint16_t *g;
+  int8_t *cm;
+  uint8_t *cv;
+  float *sm, *sr;
+  int64_t n;
+  float b1, b2, omb1, omb2, r1, r2, decay, lr, eps;
+};
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <bool ALIGNED>
+__global__ __launch_bounds__(256) void adamw8_kernel(Adamw8Args A) {
+  const int lane = (int)(threadIdx.x & 63u);
+  const int64_t nq = (A.n + kQ8Block - 1) / kQ8Block;
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  for (int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); q < nq; q += wstride) {
+    const int64_t i0 = q * kQ8Block + 4 * lane;
+    const float qm = A.sm[q] / 127.0f, qr = A.sr[q] / 255.0f;
+    float th[4], m[4], v[4];
+    bool in[4];
+    const bool full = ALIGNED && i0 + 4 <= A.n;
+    uint32_t cmw = 0, cvw = 0;
+    uint2 gw = make_uint2(0u, 0u);
+    float4 tv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (full) {
+      tv = *reinterpret_cast<const float4 *>(A.theta + i0);
+      gw = *reinterpret_cast<const uint2 *>(A.g + i0);
+      cmw = *reinterpret_cast<const uint32_t *>(A.cm + i0);
+      cvw = *reinterpret_cast<const uint32_t *>(A.cv + i0);
+    }
+    const float tt[4] = {tv.x, tv.y, tv.z, tv.w};
+    float amax = 0.f, rmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = i0 + e;
+      in[e] = i < A.n;
+      float gi = 0.f, mo = 0.f, ro = 0.f;
+      th[e] = 0.f;
+      if (full) {
+        th[e] = tt[e];
+        const uint32_t gh = (e < 2) ? gw.x : gw.y;
+        gi = (e & 1) ? __uint_as_float(gh & 0xffff0000u) : __uint_as_float(gh << 16);
+        mo = (float)(int8_t)(cmw >> (8 * e)) * qm;
+        ro = (float)((cvw >> (8 * e)) & 0xffu) * qr;
+      } else if (in[e]) {
+        th[e] = A.theta[i];
+        gi = __uint_as_float((uint32_t)A.g[i] << 16);
+        mo = (float)A.cm[i] * qm;
+        ro = (float)A.cv[i] * qr;
+      }
+      const float vo = ro * ro;
+      m[e] = A.b1 * mo + A.omb1 * gi;
+      v[e] = A.b2 * vo + A.omb2 * (gi * gi);
+      const float mh = m[e] * A.r1;
+      const float vh = v[e] * A.r2;
+      th[e] = th[e] * A.decay - A.lr * (mh / (sqrtf(vh) + A.eps));
+      if (in[e]) {
+        amax = fmaxf(amax, fabsf(m[e]));
+        rmax = fmaxf(rmax, sqrtf(v[e]));
+      }
+    }
+    amax = wave_max_f(amax);
+    rmax = wave_max_f(rmax);
+    const float im = (amax > 0.f) ? 127.0f / amax : 0.f;
+    const float ir = (rmax > 0.f) ? 255.0f / rmax : 0.f;
+    uint32_t cmo = 0, cvo = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float c = fminf(fmaxf(rintf(m[e] * im), -127.f), 127.f);
+      const float dq = fminf(rintf(sqrtf(v[e]) * ir), 255.f);
+      cmo |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
+      cvo |= ((uint32_t)dq) << (8 * e);
+    }
+    if (full) {
+      *reinterpret_cast<float4 *>(A.theta + i0) = make_float4(th[0], th[1], th[2], th[3]);
+      *reinterpret_cast<uint32_t *>(A.cm + i0) = cmo;
+      *reinterpret_cast<uint32_t *>(A.cv + i0) = cvo;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in[e]) {
+          A.theta[i0 + e] = th[e];
+          A.cm[i0 + e] = (int8_t)(cmo >> (8 * e));
+          A.cv[i0 + e] = (uint8_t)(cvo >> (8 * e));
+        }
+    }
+    if (lane == 0) {
+      A.sm[q] = amax;
+      A.sr[q] = rmax;
+    }
+  }
+}
+
+}  // namespace microadam

@@ -687,6 +687,45 @@ int ma_adamw_step(int64_t n, int64_t t, float beta1, float beta2, float eps, flo
   return MA_OK;
 }
 
+int ma_adamw8_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
+                   const uint16_t *grads, int8_t *cm, uint8_t *cv, float *sm, float *sr, hipStream_t stream) {
+  clear_error();
+  if (n < 0 || t < 1) return fail(MA_EINVAL, "ma_adamw8_step: n must be >= 0 and t >= 1");
+  if (n == 0) return MA_OK;
+  if (!theta || !grads || !cm || !cv || !sm || !sr) return fail(MA_EINVAL, "ma_adamw8_step: null pointer");
+  if (((uintptr_t)theta & 3u) || ((uintptr_t)grads & 1u) || ((uintptr_t)sm & 3u) || ((uintptr_t)sr & 3u))
+    return fail(MA_EINVAL, "ma_adamw8_step: misaligned pointer");
+  Adamw8Args a;
+  a.theta = theta;
+  a.g = grads;
+  a.cm = cm;
+  a.cv = cv;
+  a.sm = sm;
+  a.sr = sr;
+  a.n = n;
+  a.b1 = beta1;
+  a.b2 = beta2;
+  a.omb1 = (float)(1.0 - (double)beta1);
+  a.omb2 = (float)(1.0 - (double)beta2);
+  a.r1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)t)));
+  a.r2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)t)));
+  a.decay = (float)(1.0 - (double)lr * (double)wd);
+  a.lr = lr;
+  a.eps = eps;
+  // every lane's run of 4 starts at a multiple of 4 elements
+  const bool al = ((uintptr_t)theta & 15u) == 0 && ((uintptr_t)grads & 7u) == 0 && ((uintptr_t)cm & 3u) == 0 &&
+                  ((uintptr_t)cv & 3u) == 0;
+  const int64_t nq = (n + kQ8Block - 1) / kQ8Block;
+  const unsigned grid = (unsigned)std::min<int64_t>((nq + 3) / 4, 256 * 32);
+  if (al)
+    hipLaunchKernelGGL(adamw8_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(adamw8_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MA_EHIP, "ma_adamw8_step: launch failed: %s", hipGetErrorString(e));
+  return MA_OK;
+}
+
 int ma_read_state(const ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, void *host_dst) {
   clear_error();
   if (!h || !host_dst) return fail(MA_EINVAL, "ma_read_state: null argument");

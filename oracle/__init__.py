@@ -70,6 +70,9 @@ def lib():
     L.orc_block_step.argtypes = [cfgp, i64, i64, p, p, p, i64, p, p, i64, p, p]
     L.orc_adamw_step.restype = None
     L.orc_adamw_step.argtypes = [i64, i64, C.c_float, C.c_float, C.c_float, C.c_float, C.c_float, p, p, p, p]
+    L.orc_adamw8_step.restype = None
+    L.orc_adamw8_step.argtypes = [i64, i64, C.c_float, C.c_float, C.c_float, C.c_float, C.c_float,
+                                  p, p, p, p, p, p]
     L.orc_step.restype = C.c_int
     L.orc_step.argtypes = [cfgp, i64, p, p, p, p, p, p, p]
     L.orc_state_bytes.restype = u64
@@ -298,3 +301,17 @@ def adamw_step(t, theta, g_bf16, m, v, beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-4
     for a in (theta, m, v):
         assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"] and a.size == g.size
     lib().orc_adamw_step(g.size, int(t), beta1, beta2, eps, lr, wd, _ptr(theta), _ptr(g), _ptr(m), _ptr(v))
+
+Q8_BLOCK = 256
+
+
+def adamw8_step(t, theta, g_bf16, cm, cv, sm, sr, beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-4, wd=0.0):
+    """The 8-bit block-quantized AdamW baseline (orc_adamw8_step), in place:
+    theta fp32, cm int8, cv uint8 (n each), sm, sr fp32 (ceil(n/256) each)."""
+    g = np.ascontiguousarray(g_bf16, dtype=np.uint16)
+    n = g.size
+    assert theta.dtype == np.float32 and theta.size == n
+    assert cm.dtype == np.int8 and cv.dtype == np.uint8 and cm.size == n and cv.size == n
+    assert sm.dtype == np.float32 and sr.dtype == np.float32 and sm.size == sr.size == -(-n // Q8_BLOCK)
+    lib().orc_adamw8_step(n, int(t), beta1, beta2, eps, lr, wd, _ptr(theta), _ptr(g), _ptr(cm), _ptr(cv),
+                          _ptr(sm), _ptr(sr))

@@ -459,6 +459,50 @@ void orc_adamw_step(int64_t n, int64_t t, float b1, float b2, float eps, float l
     }
 }
 
+/* The 8-bit comparison optimizer (see the header for the reading). */
+void orc_adamw8_step(int64_t n, int64_t t, float b1, float b2, float eps, float lr, float wd,
+                     float *theta, const uint16_t *g, int8_t *cm, uint8_t *cv, float *sm, float *sr)
+{
+    const float omb1 = (float)(1.0 - (double)b1);
+    const float omb2 = (float)(1.0 - (double)b2);
+    const float r1 = (float)(1.0 / (1.0 - pow((double)b1, (double)t)));
+    const float r2 = (float)(1.0 / (1.0 - pow((double)b2, (double)t)));
+    const float decay = (float)(1.0 - (double)lr * (double)wd);
+    float m[ORC_Q8_BLOCK], v[ORC_Q8_BLOCK];
+    for (int64_t b0 = 0; b0 < n; b0 += ORC_Q8_BLOCK) {
+        const int64_t q = b0 / ORC_Q8_BLOCK;
+        const int64_t len = (n - b0 < ORC_Q8_BLOCK) ? n - b0 : ORC_Q8_BLOCK;
+        const float qm = sm[q] / 127.0f, qr = sr[q] / 255.0f;
+        float amax = 0.0f, rmax = 0.0f;
+        for (int64_t i = 0; i < len; ++i) {
+            const float mo = (float)cm[b0 + i] * qm;
+            const float ro = (float)cv[b0 + i] * qr;
+            const float vo = ro * ro;
+            const float gi = orc_bf16_to_f32(g[b0 + i]);
+            m[i] = b1 * mo + omb1 * gi;
+            v[i] = b2 * vo + omb2 * (gi * gi);
+            const float mh = m[i] * r1;
+            const float vh = v[i] * r2;
+            theta[b0 + i] = theta[b0 + i] * decay - lr * (mh / (sqrtf(vh) + eps));
+            if (fabsf(m[i]) > amax) amax = fabsf(m[i]);
+            if (sqrtf(v[i]) > rmax) rmax = sqrtf(v[i]);
+        }
+        sm[q] = amax;
+        sr[q] = rmax;
+        const float im = (amax > 0.0f) ? 127.0f / amax : 0.0f;
+        const float ir = (rmax > 0.0f) ? 255.0f / rmax : 0.0f;
+        for (int64_t i = 0; i < len; ++i) {
+            float c = rintf(m[i] * im);
+            if (c > 127.0f) c = 127.0f;
+            if (c < -127.0f) c = -127.0f;
+            cm[b0 + i] = (int8_t)c;
+            float d = rintf(sqrtf(v[i]) * ir);
+            if (d > 255.0f) d = 255.0f;
+            cv[b0 + i] = (uint8_t)d;
+        }
+    }
+}
+
 uint64_t orc_state_bytes(const orc_cfg *c)
 {
     return (uint64_t)((c->d + 1) / 2) + 4ull * (uint64_t)c->m * (uint64_t)c->k;

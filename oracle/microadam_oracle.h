@@ -104,6 +104,19 @@ int orc_step(const orc_cfg *c, int64_t t, float *theta, const uint16_t *g,
 void orc_adamw_step(int64_t n, int64_t t, float b1, float b2, float eps, float lr, float wd,
                     float *theta, const uint16_t *g, float *m, float *v);
 
+/* ---- comparison baseline: 8-bit block-quantized AdamW (the second
+ * paragraph's 2d-byte optimizer).  Reading (the page fixes no 8-bit scheme):
+ * blocks of ORC_Q8_BLOCK elements, each with two fp32 scales; m as int8 codes
+ * c = rint(m * (127/sm)) with sm = max|m| of the block, m~ = c * (sm/127); v as
+ * uint8 codes of sqrt(v): c = rint(sqrt(v) * (255/sr)) with sr = max sqrt(v),
+ * v~ = (c * (sr/255))^2.  One step: dequantize, the AdamW recurrence and
+ * parameter update of orc_adamw_step on the dequantized moments, then
+ * requantize the new moments with the block's new scales (a zero block gets
+ * scale 0 and codes 0).  cm: int8[n], cv: uint8[n], sm, sr: float[ceil(n/B)]. */
+#define ORC_Q8_BLOCK 256
+void orc_adamw8_step(int64_t n, int64_t t, float b1, float b2, float eps, float lr, float wd,
+                     float *theta, const uint16_t *g, int8_t *cm, uint8_t *cv, float *sm, float *sr);
+
 /* array helpers */
 void orc_bf16_rne_array(const float *x, int64_t n, uint16_t *out);
 void orc_pcg_hash_array(const uint32_t *x, int64_t n, uint32_t *out);

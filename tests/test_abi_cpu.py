@@ -77,3 +77,11 @@ def test_adamw_argument_checks_without_gpu():
     assert lib.ma_adamw_step(10, 0, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_EINVAL
     assert lib.ma_adamw_step(0, 1, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_OK
     assert lib.ma_adamw_step(10, 1, 0.9, 0.999, 1e-8, 1e-3, 0.0, None, None, None, None, None) == L.MA_EINVAL
+
+
+def test_adamw8_argument_checks_without_gpu():
+    lib = L.lib()
+    args = (0.9, 0.999, 1e-8, 1e-3, 0.0)
+    assert lib.ma_adamw8_step(-1, 1, *args, None, None, None, None, None, None, None) == L.MA_EINVAL
+    assert lib.ma_adamw8_step(0, 1, *args, None, None, None, None, None, None, None) == L.MA_OK
+    assert lib.ma_adamw8_step(5, 1, *args, None, None, None, None, None, None, None) == L.MA_EINVAL

@@ -46,3 +46,29 @@ def test_adamw_matches_oracle(n, misalign, wd):
         assert_bits_equal(f"adamw theta t={t}", th_d.cpu().numpy(), th)
         assert_bits_equal(f"adamw m t={t}", m_d.cpu().numpy(), m)
         assert_bits_equal(f"adamw v t={t}", v_d.cpu().numpy(), v)
+
+
+@pytest.mark.parametrize("n,misalign,wd", [(1, False, 0.0), (255, False, 0.1), (256 * 5, False, 0.0),
+                                           (1_000_003, False, 0.01), (100_001, True, 0.01)])
+def test_adamw8_matches_oracle(n, misalign, wd):
+    from memory_compressed_adaptive_amd.baselines import Q8_BLOCK, adamw8_step
+    rng = np.random.default_rng(n + 1)
+    nq = -(-n // Q8_BLOCK)
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    cm = np.zeros(n, np.int8)
+    cv = np.zeros(n, np.uint8)
+    sm = np.zeros(nq, np.float32)
+    sr = np.zeros(nq, np.float32)
+    d_th, d_cm, d_cv = _dev(th, misalign), _dev(cm, misalign), _dev(cv, misalign)
+    d_sm, d_sr = _dev(sm, False), _dev(sr, False)
+    for t in range(1, 6):
+        g = O.bf16_rne((rng.standard_normal(n) * 10.0 ** rng.uniform(-4, -2)).astype(np.float32))
+        say(f"[adamw8] n={n} misalign={misalign} wd={wd} step {t}")
+        adamw8_step(d_th, _dev(g.view(np.int16), misalign), d_cm, d_cv, d_sm, d_sr, t, lr=1e-3, wd=wd)
+        torch.cuda.synchronize()
+        O.adamw8_step(t, th, g, cm, cv, sm, sr, lr=1e-3, wd=wd)
+        assert_bits_equal(f"adamw8 theta t={t}", d_th.cpu().numpy(), th)
+        assert_bits_equal(f"adamw8 cm t={t}", d_cm.cpu().numpy(), cm)
+        assert_bits_equal(f"adamw8 cv t={t}", d_cv.cpu().numpy(), cv)
+        assert_bits_equal(f"adamw8 sm t={t}", d_sm.cpu().numpy(), sm)
+        assert_bits_equal(f"adamw8 sr t={t}", d_sr.cpu().numpy(), sr)

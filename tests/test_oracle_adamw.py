@@ -66,3 +66,58 @@ def test_adamw_matches_double_recurrence():
         scale = np.maximum(np.abs(x), step).astype(np.float32)
         assert np.all(np.abs(th - ref) <= 4e-6 * step + 4 * np.spacing(scale).astype(np.float64))
         M, V = m.astype(np.float64), v.astype(np.float64)   # follow the fp32 moments
+
+
+def _deq(cm, cv, sm, sr):
+    q = np.repeat(np.arange(sm.size), O.Q8_BLOCK)[:cm.size]
+    qm = (sm / np.float32(127.0)).astype(np.float32)[q]
+    qr = (sr / np.float32(255.0)).astype(np.float32)[q]
+    ro = (cv.astype(np.float32) * qr).astype(np.float32)
+    return (cm.astype(np.float32) * qm).astype(np.float32), (ro * ro).astype(np.float32), qm, qr
+
+
+def test_adamw8_is_adamw_on_the_dequantized_moments():
+    # the step equals the fp32 AdamW step (pinned above) applied to the
+    # dequantized moments; the new moments are then within half a code step
+    rng = np.random.default_rng(7)
+    n = 3 * O.Q8_BLOCK + 77
+    th = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    nq = -(-n // O.Q8_BLOCK)
+    cm = np.zeros(n, np.int8)
+    cv = np.zeros(n, np.uint8)
+    sm = np.zeros(nq, np.float32)
+    sr = np.zeros(nq, np.float32)
+    for t in range(1, 9):
+        g = O.bf16_rne((rng.standard_normal(n) * 10.0 ** rng.uniform(-4, -2)).astype(np.float32))
+        m0, v0, _, _ = _deq(cm, cv, sm, sr)
+        th_ref, m_ref, v_ref = th.copy(), m0.copy(), v0.copy()
+        O.adamw_step(t, th_ref, g, m_ref, v_ref, lr=1e-3, wd=0.01)
+        O.adamw8_step(t, th, g, cm, cv, sm, sr, lr=1e-3, wd=0.01)
+        assert np.array_equal(th.view(np.uint32), th_ref.view(np.uint32)), t
+        # scales are the block maxima of the new moments
+        for q in range(nq):
+            sl = slice(q * O.Q8_BLOCK, min(n, (q + 1) * O.Q8_BLOCK))
+            assert sm[q] == np.abs(m_ref[sl]).max()
+            assert sr[q] == np.sqrt(v_ref[sl]).max()
+            assert np.abs(cm[sl]).max() == 127 and cv[sl].max() == 255
+        m1, v1, qm, qr = _deq(cm, cv, sm, sr)
+        # half a code step, plus the rounding of the fp32 scales (|code| * 2 ulp <= 3e-5 step)
+        assert np.all(np.abs(m1.astype(np.float64) - m_ref) <= 0.5 * qm * (1 + 1e-4))
+        r1 = (cv.astype(np.float32) * qr).astype(np.float64)   # the dequantized sqrt(v)
+        assert np.all(np.abs(r1 - np.sqrt(v_ref)) <= 0.5 * qr * (1 + 1e-4) + 1e-30)
+
+
+def test_adamw8_rounds_to_nearest_not_toward_zero():
+    # a planted truncation would put codes up to a whole step off; nearest
+    # rounding keeps the mean code error near zero
+    rng = np.random.default_rng(9)
+    n = 64 * O.Q8_BLOCK
+    th = np.zeros(n, np.float32)
+    cm, cv = np.zeros(n, np.int8), np.zeros(n, np.uint8)
+    sm, sr = np.zeros(n // O.Q8_BLOCK, np.float32), np.zeros(n // O.Q8_BLOCK, np.float32)
+    g = O.bf16_rne(rng.standard_normal(n).astype(np.float32))
+    O.adamw8_step(1, th, g, cm, cv, sm, sr)
+    m_true = (np.float32(1 - np.float32(0.9)) * O.bf16_to_f32(g)).astype(np.float32)
+    m1, _, qm, _ = _deq(cm, cv, sm, sr)
+    err = (m1 - m_true) / qm
+    assert abs(err.mean()) < 0.02 and np.abs(err).max() <= 0.5 + 1e-4
