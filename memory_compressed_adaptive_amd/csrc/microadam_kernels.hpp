@@ -326,7 +326,9 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   // instead of being hoisted out of the loop and held in (spilled) registers.
   int tid = (int)threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, wv = tid >> 6;
+  __builtin_assume(tid >= 0 && tid < kThreads);
+  // the wave index is uniform: a scalar register
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---------------- ef_dequant_accumulate: a = f32(g) + fmaf(code, step, delta)
   float lo = 0.f, step = 0.f;
@@ -465,6 +467,8 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
         // the tie cut in index order, and the ordered write of (I, bf16(V))
         // into the window row (ring_write).
         if (wv == 0) {
+          // the serial part of the block: ahead of the other waves on its SIMD
+          __builtin_amdgcn_s_setprio(3);
           const int R = ((int)C + 63) >> 6;
           uint32_t ck[kCandMax / 64];
           uint32_t kmax = 0;
@@ -558,6 +562,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
             sm.sel[1] = (uint32_t)last;
             sm.sel[2] = (cut || ntie == need) ? 1u : 0u;
           }
+          __builtin_amdgcn_s_setprio(0);
         } else {
           // the other waves, meanwhile: the quantizer's random words and the
           // bitmap of the window's other rows
@@ -936,7 +941,11 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
   uint16_t *s_pos = sm.pos;
   uint32_t *s_cnt = sm.cnt;
 
-  const int tid = (int)threadIdx.x;
+  // thread-derived addresses are recomputed here rather than carried over
+  // (in registers, or spilled) from the compressor of the fused kernel
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  __builtin_assume(tid >= 0 && tid < kThreads);
   const int64_t s = j * (int64_t)A.B;
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
   const int64_t off = A.off_tab[j];
