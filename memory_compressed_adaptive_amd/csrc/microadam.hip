@@ -35,8 +35,10 @@ void clear_error() {
   g_msg[0] = 0;
 }
 
-// Largest LDS the update kernel asks for: two of its workgroups fit one CU.
-constexpr size_t kApplyLdsLimit = 64 * 1024;
+// Largest dynamic LDS the update kernel asks for: two of its workgroups, with
+// their static LDS, still fit one CU's 160 KiB (79 KiB each), so a long window
+// (m = 37 at k = d/100) keeps every touched slot of a block in one pass.
+constexpr size_t kApplyLdsLimit = 79 * 1024;
 
 }  // namespace
 

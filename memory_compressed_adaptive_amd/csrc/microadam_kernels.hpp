@@ -959,12 +959,36 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
     __syncthreads();
   }
 
-  // ---------------- the block's window entries: one pass over global memory
-  // (8 rows in flight per thread), copied to LDS when they fit; union bitmap.
-  // A zero value adds nothing (unwritten rows are all zero); an index outside
+  // ---------------- the block's window entries and their union bitmap.  A
+  // zero value adds nothing (unwritten rows are all zero); an index outside
   // the block (only possible in an imported state) is ignored.
   // (PRELOADED: the entries and the bitmap are already complete)
-  for (int i0 = 0; !PRELOADED && i0 < M; i0 += 8) {
+  // Entries that fit in LDS: every thread DMAs its share of the m * k_b
+  // entries straight to LDS, all in flight at once (one memory round trip),
+  // then the bitmap is built from LDS.  Otherwise one pass over global memory
+  // with 8 rows in flight per thread builds the bitmap, and the rows are read
+  // again from global memory when they are added.
+  const bool win_dma = !PRELOADED && in_lds;
+  if (win_dma) {
+    const int tot = M * kb;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int x0 = wv * 64; x0 < tot; x0 += kThreads) {
+      const int x = x0 + lane;
+      if (x < tot) {
+        const int i = x / kb, q = x - i * kb;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.G + (int64_t)i * A.k + off + q),
+                                         (lds_void_t *)(&s_ent[x0]), 4, 0, 0);
+      }
+    }
+    wait_vm_all();
+    __syncthreads();
+    for (int x = tid; x < tot; x += kThreads) {
+      const uint32_t e = s_ent[x];
+      if ((e & 0x7fff0000u) && (int)(e & 0xffffu) < L)
+        atomicOr(&s_bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+    }
+  }
+  for (int i0 = 0; !PRELOADED && !win_dma && i0 < M; i0 += 8) {
     for (int q = tid; q < kb; q += kThreads) {
       uint32_t e[8];
 #pragma unroll
