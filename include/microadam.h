@@ -79,8 +79,9 @@ enum {
  * b-bit error quantizer; AdamW hyperparameters beta1, beta2, eps, lr, wd;
  * seed keys the quantizer's counter-based random numbers on (seed, step,
  * element)).  Requires d >= 1, 1 <= B_d <= 32766, 0 <= k <= d, m >= 1,
- * 0 <= beta < 1, eps > 0, finite lr and wd >= 0; b must be 4
- * (MA_EUNSUPPORTED otherwise).  Allocates and zero-fills all state on the
+ * 0 <= beta < 1, eps > 0, finite lr and wd >= 0; b must be 4 and m at
+ * most 1024 (MA_EUNSUPPORTED otherwise: the update keeps the window's decay
+ * factors in LDS).  Allocates and zero-fills all state on the
  * current HIP device (so e_1 = 0 and unwritten window rows add nothing);
  * step count t = 0.  Returns NULL on error.
  */

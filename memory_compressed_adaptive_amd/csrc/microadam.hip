@@ -36,9 +36,9 @@ void clear_error() {
 }
 
 // Largest dynamic LDS the update kernel asks for: two of its workgroups, with
-// their static LDS, still fit one CU's 160 KiB (79 KiB each), so a long window
+// their static LDS (under 1 KiB), still fit one CU's 160 KiB, so a long window
 // (m = 37 at k = d/100) keeps every touched slot of a block in one pass.
-constexpr size_t kApplyLdsLimit = 79 * 1024;
+constexpr size_t kApplyLdsLimit = 79 * 1024 - 512;
 
 }  // namespace
 
@@ -332,6 +332,10 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
   if (B_d < 1 || B_d >= 32767) { fail(MA_EINVAL, "B_d must be in [1, 32766] (got %d)", B_d); return nullptr; }
   if (k < 0 || k > d) { fail(MA_EINVAL, "k must be in [0, d] (got %lld)", (long long)k); return nullptr; }
   if (m < 1) { fail(MA_EINVAL, "m must be >= 1 (got %d)", m); return nullptr; }
+  if (m > kMaxWindow) {
+    fail(MA_EUNSUPPORTED, "windows of more than %d rows are not built (got m = %d)", kMaxWindow, m);
+    return nullptr;
+  }
   if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f)) {
     fail(MA_EINVAL, "betas must be in [0, 1)");
     return nullptr;
@@ -367,16 +371,18 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     bp[(size_t)m + r] = (float)std::pow((double)beta2, (double)r);
   }
   // The update kernel's LDS: bitmap and slot bases (8 bytes per 32 positions),
-  // the block's window entries when they fit in 5/8 of the budget (the rows
-  // are then read from global memory once, not once per row pass), and
-  // 10 bytes per slot for at most min(B_d, m*kb_max) touched positions.
+  // the decay factors (8 bytes per window row), the block's window entries
+  // when they fit in 5/8 of the budget (the rows are then read from global
+  // memory once, not once per row pass), and 10 bytes per slot for at most
+  // min(B_d, m*kb_max) touched positions.
   const int W = h->cpt * kChunkSpan / 32;
   const int64_t ents = (int64_t)m * kb_max;
   h->ent_cap = (4 * ents <= (int64_t)kApplyLdsLimit * 5 / 8) ? (int)ents : 0;
   const int64_t umax = std::min<int64_t>((int64_t)B_d, ents);
-  const int64_t cap_limit = ((int64_t)kApplyLdsLimit - 8 * (int64_t)W - 4 * (int64_t)h->ent_cap) / 10;
+  const int64_t cap_limit =
+      ((int64_t)kApplyLdsLimit - 8 * (int64_t)W - 8 * (int64_t)m - 4 * (int64_t)h->ent_cap) / 10;
   h->cap = (int)std::max<int64_t>(1, std::min<int64_t>(umax, cap_limit));
-  h->apply_lds = 8 * (size_t)W + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
+  h->apply_lds = 8 * (size_t)W + 8 * (size_t)m + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
   // expected fraction of positions present in a full window: 1 - (1 - k/d)^m
   h->dense_default = false;   // measured: gathering touched parameters wins at m = 1 and m = 10
   // fused kernel: full 4096-element chunks, CPT <= 4, and the m window rows

@@ -906,7 +906,9 @@ __device__ __forceinline__ void st_param(const ApplyArgs &A, int64_t i, float v)
   else
     A.theta[i] = v;
 }
-constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
+constexpr int kThetaPerThread = 8;
+constexpr int kMaxWindow = 1024;     // window rows the update kernels take (their factors sit in LDS)
+constexpr int kFusedBeta = 64;       // decay factors of the fused kernel (m <= kFusedEnt / 64 rows)   // parameters a thread holds in flight in the sparse update
 constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over
 
 // LDS of the update: bitmap of touched positions (W words), per-word slot
@@ -915,12 +917,32 @@ constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is sp
 // per pass; cnt holds kWaves + 1 words.
 struct ApplySmem {
   uint32_t *bits, *wbase, *ent;
+  float *beta;   // the 2m decay factors, staged in LDS
   float *z1, *z2;
   uint16_t *pos;
   uint32_t *cnt;
   int cap, ent_stride;
   bool in_lds;
 };
+
+// A decay factor from the LDS table, read through an LDS-typed pointer (a
+// generic load would be counted with vector memory, and waiting for it would
+// also wait for the parameter loads in flight).
+typedef __attribute__((address_space(3))) float lds_float_t;
+__device__ __forceinline__ float decay_factor(const float *beta, int idx) {
+  return ((const lds_float_t *)beta)[idx];
+}
+
+// Issues the LDS-DMA of the 2m decay factors into beta.  The caller waits for
+// its vector memory and a barrier before the table is read.
+__device__ __forceinline__ void stage_beta(const ApplyArgs &A, float *beta, int tid) {
+  const int n = 2 * A.m;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int w0 = wv * 64; w0 < n; w0 += kThreads)
+    if (w0 + lane < n)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.betapow + w0 + lane),
+                                       (lds_void_t *)(beta + w0), 4, 0, 0);
+}
 
 // The update of block j.
 // MODE 0: only touched parameters are read and written (decay must be 1).
@@ -968,6 +990,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
   // then the bitmap is built from LDS.  Otherwise one pass over global memory
   // with 8 rows in flight per thread builds the bitmap, and the rows are read
   // again from global memory when they are added.
+  if (!PRELOADED) stage_beta(A, sm.beta, tid);
   const bool win_dma = !PRELOADED && in_lds;
   if (win_dma) {
     const int tot = M * kb;
@@ -1004,7 +1027,10 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       }
     }
   }
-  if (!PRELOADED) __syncthreads();
+  if (!PRELOADED) {
+    wait_vm_all();   // the decay factors' DMA (the window DMA is waited for above)
+    __syncthreads();
+  }
 
   // ---------------- compact slots: slot(p) = number of touched positions below p
   uint32_t wc[WPT], mine = 0;
@@ -1136,7 +1162,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
           if (i < M) {
             int r = A.tm - i;
             if (r < 0) r += M;
-            const float f1 = A.betapow[r], f2 = A.betapow[M + r];
+            const float f1 = decay_factor(sm.beta, r), f2 = decay_factor(sm.beta, M + r);
             if (slv[u] < n) {
               s_z1[slv[u]] = s_z1[slv[u]] + f1 * vv[u];
               s_z2[slv[u]] = s_z2[slv[u]] + f2 * (vv[u] * vv[u]);
@@ -1149,7 +1175,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
     for (int i = 0; !(in_lds && kb <= kThreads) && i < M; ++i) {
       int r = A.tm - i;
       if (r < 0) r += M;
-      const float f1 = A.betapow[r], f2 = A.betapow[M + r];
+      const float f1 = decay_factor(sm.beta, r), f2 = decay_factor(sm.beta, M + r);
       for (int q = tid; q < kb; q += kThreads) {
         const uint32_t e = in_lds ? s_ent[i * es + q] : A.G[(int64_t)i * A.k + off + q];
         const uint32_t I = e & 0xffffu;
@@ -1250,7 +1276,8 @@ __device__ __forceinline__ ApplySmem apply_smem(const ApplyArgs &A, uint32_t *sm
   ApplySmem sm;
   sm.bits = smem;
   sm.wbase = smem + W;
-  sm.ent = smem + 2 * W;
+  sm.beta = reinterpret_cast<float *>(smem + 2 * W);
+  sm.ent = smem + 2 * W + 2 * A.m;
   sm.z1 = reinterpret_cast<float *>(sm.ent + A.ent_cap);
   sm.z2 = sm.z1 + A.cap;
   sm.pos = reinterpret_cast<uint16_t *>(sm.z2 + A.cap);
@@ -1306,6 +1333,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   __shared__ uint32_t ent[kFusedEnt];
+  __shared__ float s_beta[kFusedBeta];
+  static_assert(2 * (kFusedEnt / 64) <= kFusedBeta, "the fused kernel's decay factors fit");
   static_assert(sizeof(FullBlockStage<CPT>) >= 4u * (CPT * kChunkSpan / 2) + 8u * (CPT * kChunkSpan / 32),
                 "random words, bitmap and slot bases fit the staging space");
   const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
@@ -1327,6 +1356,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
                                        (lds_void_t *)(&ent[i * es + q0]), 4, 0, 0);
     }
   }
+  // the decay factors, waited for with the staged inputs
+  stage_beta(A, s_beta, tid);
   // LDS of the staged inputs, once they are consumed: the quantizer's random
   // words (L/2 words), then the bitmap and slot bases; the update's per-slot
   // arrays later reuse the random words' space
@@ -1354,6 +1385,7 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   as.cnt = sm.cnt;
   as.ent_stride = es;
   as.in_lds = true;
+  as.beta = s_beta;
   apply_block<CPT, kModeSparse, false, true, BF>(A, j, 0, as);
 }
 

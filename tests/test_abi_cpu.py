@@ -48,6 +48,7 @@ def test_synth_library_loads():
     ((100, 64, 1, 10, 4, 0.9, 0.999, 1e-8, 1e-4, -1.0, 42), L.MA_EINVAL),        # wd < 0
     ((100, 64, 1, 10, 8, 0.9, 0.999, 1e-8, 1e-4, 0.0, 42), L.MA_EUNSUPPORTED),   # b = 8
     ((100, 64, 1, 10, 2, 0.9, 0.999, 1e-8, 1e-4, 0.0, 42), L.MA_EUNSUPPORTED),   # b = 2
+    ((100, 64, 1, 1025, 4, 0.9, 0.999, 1e-8, 1e-4, 0.0, 42), L.MA_EUNSUPPORTED),  # m > 1024
 ])
 def test_create_rejects_invalid_arguments(args, code):
     lib = L.lib()
