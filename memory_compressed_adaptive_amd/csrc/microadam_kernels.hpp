@@ -923,6 +923,8 @@ struct ApplySmem {
   uint32_t *cnt;
   int cap, ent_stride;
   bool in_lds;
+  int64_t off;   // PRELOADED: the block's window offset and k_b, already known
+  int kb;
 };
 
 // A decay factor from the LDS table, read through an LDS-typed pointer (a
@@ -970,8 +972,8 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
   __builtin_assume(tid >= 0 && tid < kThreads);
   const int64_t s = j * (int64_t)A.B;
   const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
-  const int64_t off = A.off_tab[j];
-  const int kb = (int)(A.off_tab[j + 1] - off);
+  const int64_t off = PRELOADED ? sm.off : A.off_tab[j];
+  const int kb = PRELOADED ? sm.kb : (int)(A.off_tab[j + 1] - off);
   const int M = A.m;
   const bool in_lds = PRELOADED || sm.in_lds;
   const int es = PRELOADED ? sm.ent_stride : kb;   // LDS row stride of the entries
@@ -1051,9 +1053,6 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       b += wc[r];
     }
   }
-  // spread over kTouchedSlots counters so the blocks do not contend
-  if (MODE != kModeMoments && A.touched && tid == 0)
-    atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
 
   if (MODE == kModeMoments) {
 #pragma unroll
@@ -1094,12 +1093,16 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
     __syncthreads();
     // the touched parameters of this pass, loaded before the row scatter so
     // their latency overlaps it
+    // (Every load is issued, lanes past the pass re-loading its last slot,
+    // and every loaded value is used: a register cleared instead, or a load
+    // waited for on one path only, makes the compiler wait for all vector
+    // memory, the compressor's stores included, at the next pass.)
     float thv[kThetaPerThread];
     if (MODE == kModeSparse) {
 #pragma unroll
       for (int u = 0; u < kThetaPerThread; ++u) {
-        const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
-        thv[u] = (x < n) ? ld_param<BF>(A, s + s_pos[x]) : 0.f;
+        const uint32_t x = min((uint32_t)tid + (uint32_t)(u * kThreads), n - 1u);
+        thv[u] = ld_param<BF>(A, s + s_pos[x]);
       }
     }
     // dense: the thread's 8 consecutive parameters of each chunk, streamed
@@ -1194,10 +1197,12 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
 #pragma unroll
       for (int u = 0; u < kThetaPerThread; ++u) {
         const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+        const float th = thv[u];
+        asm volatile("" ::"v"(th));   // the wait for the load, on every path
         if (x < n) {
           const float mh = A.c1 * s_z1[x];
           const float vh = A.c2 * s_z2[x];
-          st_param<BF>(A, s + s_pos[x], thv[u] - A.lr * (mh / (sqrtf(vh) + A.eps)));
+          st_param<BF>(A, s + s_pos[x], th - A.lr * (mh / (sqrtf(vh) + A.eps)));
         }
       }
     } else if (MODE == kModeDense) {
@@ -1255,7 +1260,9 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
           }
         }
     }
-    __syncthreads();
+    // the next pass reuses the slot arrays; after the last pass no barrier
+    // (it would wait for the parameter stores to complete)
+    if (s0 + pass < U) __syncthreads();
   }
   if (MODE == kModeDense && U == 0 && A.decay != 1.0f) {
     // nothing touched: the decay alone
@@ -1267,6 +1274,11 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         if (i0 + e < L) st_param<BF>(A, s + i0 + e, ld_param<BF>(A, s + i0 + e) * A.decay);
     }
   }
+  // the touched count, spread over kTouchedSlots counters so the blocks do
+  // not contend; issued after the block's last barrier, which would
+  // otherwise wait for the atomic to complete
+  if (MODE != kModeMoments && A.touched && tid == 0)
+    atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
 }
 
 // LDS of the standalone update: dynamic, laid out as in ApplySmem.
@@ -1386,6 +1398,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   as.ent_stride = es;
   as.in_lds = true;
   as.beta = s_beta;
+  as.off = in.off;
+  as.kb = in.kb;
   apply_block<CPT, kModeSparse, false, true, BF>(A, j, 0, as);
 }
 
