@@ -211,6 +211,12 @@ def test_long_window_multi_pass_slots():
     full_parity("m=37 k=d/10", 40_000, 16384, 4_000, 37, 40, moments=True)
 
 
+@pytest.mark.parametrize("m,steps", [(200, 206), (1024, 1030)])
+def test_long_windows_up_to_the_limit(m, steps):
+    # 2m decay factors staged in LDS by several waves; the window wraps
+    full_parity(f"m={m}", 3_000, 1024, 30, m, steps, moments=False)
+
+
 def test_run_twice_is_bitwise_deterministic():
     runs = []
     for _ in range(2):
