@@ -769,7 +769,10 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
     }
     if (ALIGNED) {
       // element s + i0 starts code word (s + i0) / 8 of the block's aligned run
-      if (FULL || i0 < L) reinterpret_cast<uint32_t *>(A.ef + (s >> 1))[c * kThreads + tid] = packed;
+      // a streaming store (non-temporal): nothing reads the codes again this
+      // step, and L2 keeps the lines the update will write instead
+      if (FULL || i0 < L)
+        __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(A.ef + (s >> 1)) + c * kThreads + tid);
     } else {
       // neighbouring blocks (and threads) may share a code byte: change only
       // this element's nibble, by xor-ing old ^ new into its 32-bit word
@@ -904,7 +907,7 @@ __device__ __forceinline__ void st_param(const ApplyArgs &A, int64_t i, float v)
   if (BF)
     A.theta16[i] = (uint16_t)f32_to_bf16_rne(v);
   else
-    A.theta[i] = v;
+    __builtin_nontemporal_store(v, A.theta + i);   // streaming: not read again this step
 }
 constexpr int kThetaPerThread = 8;
 constexpr int kMaxWindow = 1024;     // window rows the update kernels take (their factors sit in LDS)
