@@ -33,6 +33,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 8;                       // consecutive elements per thread
 constexpr int kChunkSpan = kThreads * kChunk;   // 4096 elements per chunk
 constexpr int kCandMax = 512;                   // candidates one wave selects from (8 per lane)
+constexpr int kCacheStream = 2;                // cache-policy bits of a non-temporal (streaming) access
 constexpr int kCoarseLowBit = 16;               // candidate threshold keeps key bits 30..16
 #ifndef MA_FULL_WAVES
 #define MA_FULL_WAVES 6   // 80 VGPRs: three 512-thread blocks per CU
@@ -275,13 +276,15 @@ __device__ __forceinline__ void stage_full_block(const CompressArgs &A, int64_t 
   // uniform block bases plus 32-bit lane offsets (scalar-base addressing)
   const u32x4 *gb = reinterpret_cast<const u32x4 *>(A.g + s);
   const uint32_t *eb = reinterpret_cast<const uint32_t *>(A.ef + (s >> 1));
+  // the codes are streamed (non-temporal): the quantizer overwrites them with
+  // streaming stores, and nothing else reads them this step
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(gb + (c * kThreads + tid)),
                                      (lds_void_t *)(&st.g[c][wbase]), 16, 0, 0);
     if (EF)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(eb + (c * kThreads + tid)),
-                                       (lds_void_t *)(&st.ef[c][wbase]), 4, 0, 0);
+                                       (lds_void_t *)(&st.ef[c][wbase]), 4, 0, kCacheStream);
   }
   in.lo = EF ? A.stats[2 * j] : 0.f;
   in.hi = EF ? A.stats[2 * j + 1] : 0.f;
@@ -1357,7 +1360,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   stage_full_block<CPT, EF>(C, j, st, in);
 
   // window rows other than row t mod m, into ent[i * es ..] (whole waves; the
-  // lanes past k_b re-read the segment's last entry into the row's padding)
+  // lanes past k_b re-read the segment's last entry into the row's padding);
+  // streaming loads, measured slightly faster
   int tid = (int)threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int es = (in.kb + 63) & ~63;
@@ -1368,7 +1372,7 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
       if (i == A.tm) continue;
       const int q = min(q0 + (tid & 63), in.kb - 1);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.G + (int64_t)i * A.k + in.off + q),
-                                       (lds_void_t *)(&ent[i * es + q0]), 4, 0, 0);
+                                       (lds_void_t *)(&ent[i * es + q0]), 4, 0, kCacheStream);
     }
   }
   // the decay factors, waited for with the staged inputs
