@@ -1008,7 +1008,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       if (x < tot) {
         const int i = x / kb, q = x - i * kb;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.G + (int64_t)i * A.k + off + q),
-                                         (lds_void_t *)(&s_ent[x0]), 4, 0, 0);
+                                         (lds_void_t *)(&s_ent[x0]), 4, 0, kCacheStream);
       }
     }
     wait_vm_all();
