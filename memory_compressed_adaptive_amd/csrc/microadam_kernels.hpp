@@ -907,10 +907,11 @@ __device__ __forceinline__ float ld_param(const ApplyArgs &A, int64_t i) {
 }
 template <bool BF>
 __device__ __forceinline__ void st_param(const ApplyArgs &A, int64_t i, float v) {
+  // streaming stores: nothing reads the parameters again this step
   if (BF)
-    A.theta16[i] = (uint16_t)f32_to_bf16_rne(v);
+    __builtin_nontemporal_store((uint16_t)f32_to_bf16_rne(v), A.theta16 + i);
   else
-    __builtin_nontemporal_store(v, A.theta + i);   // streaming: not read again this step
+    __builtin_nontemporal_store(v, A.theta + i);
 }
 constexpr int kThetaPerThread = 8;
 constexpr int kMaxWindow = 1024;     // window rows the update kernels take (their factors sit in LDS)
