@@ -35,10 +35,12 @@ void clear_error() {
   g_msg[0] = 0;
 }
 
-// Largest dynamic LDS the update kernel asks for: two of its workgroups, with
-// their static LDS (under 1 KiB), still fit one CU's 160 KiB, so a long window
-// (m = 37 at k = d/100) keeps every touched slot of a block in one pass.
-constexpr size_t kApplyLdsLimit = 79 * 1024 - 512;
+// Largest dynamic LDS the update kernel asks for: three of its workgroups,
+// with their static LDS (under 1 KiB), fit one CU's 160 KiB.  A long window
+// (m = 37 at k = d/100) then takes two slot passes per block; measured, that
+// beats one pass at two workgroups per CU (and smaller budgets, with more
+// passes, are slower again).
+constexpr size_t kApplyLdsLimit = 53 * 1024 - 512;
 
 }  // namespace
 
