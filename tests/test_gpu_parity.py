@@ -175,6 +175,8 @@ def test_global_quantizer_single_block_equals_block_mode():
     (70_000, 16384, 700, 4, 0.1, 0, False),                    # decay: dense update, 16-byte rows
     (70_000, 16384, 700, 4, 0.1, 0, True),                     # decay, parameters 2 bytes off
     (20_011, 1003, 500, 3, 0.0, 0, False),                     # odd B_d
+    (100_003, 16384, 1000, 4, 0.0, L.MA_FLAG_GLOBAL_QUANT, False),  # one (delta, Delta) over all d
+    (60_000, 16384, 6000, 37, 0.0, 0, False),                  # window too large for LDS: rows from HBM
 ])
 def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
     # ma_step_bf16: widen, fp32 step, round to nearest even once
@@ -183,7 +185,8 @@ def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
     th16 = O.bf16_rne((rng.standard_normal(d) * 0.02).astype(np.float32))
     opt = MicroAdam(d, B, k, m, lr=lr, wd=wd)
     opt.set_flags(flags)
-    orc = O.FullState(O.make_cfg(d, B, k, m, 4, 0.9, 0.999, 1e-8, lr, wd, 42, 0))
+    orc = O.FullState(O.make_cfg(d, B, k, m, 4, 0.9, 0.999, 1e-8, lr, wd, 42,
+                                 O.FLAG_GLOBAL_QUANT if flags & L.MA_FLAG_GLOBAL_QUANT else 0))
     th_cpu = th16.copy()
     if misalign:
         buf = torch.empty(d + 1, dtype=torch.int16, device="cuda")
