@@ -96,30 +96,31 @@ struct ma_ctx {
 namespace {
 
 void free_all(ma_ctx *h) {
+  // teardown: failures are ignored on purpose (nothing is left to undo)
   if (!h) return;
-  hipFree(h->codes);
-  hipFree(h->stats);
-  hipFree(h->window);
-  hipFree(h->off_tab);
-  hipFree(h->betapow);
-  hipFree(h->touched);
-  hipFree(h->deferred);
-  hipFree(h->n_deferred);
-  hipFree(h->blkmm);
-  hipFree(h->selinfo);
-  hipFree(h->gmm);
+  (void)hipFree(h->codes);
+  (void)hipFree(h->stats);
+  (void)hipFree(h->window);
+  (void)hipFree(h->off_tab);
+  (void)hipFree(h->betapow);
+  (void)hipFree(h->touched);
+  (void)hipFree(h->deferred);
+  (void)hipFree(h->n_deferred);
+  (void)hipFree(h->blkmm);
+  (void)hipFree(h->selinfo);
+  (void)hipFree(h->gmm);
   for (auto &ev : h->events) {
-    hipEventDestroy(ev.start);
-    hipEventDestroy(ev.end);
+    (void)hipEventDestroy(ev.start);
+    (void)hipEventDestroy(ev.end);
   }
-  for (auto e : h->pool) hipEventDestroy(e);
+  for (auto e : h->pool) (void)hipEventDestroy(e);
   h->events.clear();
   h->pool.clear();
-  for (auto e : h->chunk_ev) hipEventDestroy(e);
+  for (auto e : h->chunk_ev) (void)hipEventDestroy(e);
   h->chunk_ev.clear();
-  if (h->fork_ev) hipEventDestroy(h->fork_ev);
-  if (h->join_ev) hipEventDestroy(h->join_ev);
-  if (h->side) hipStreamDestroy(h->side);
+  if (h->fork_ev) (void)hipEventDestroy(h->fork_ev);
+  if (h->join_ev) (void)hipEventDestroy(h->join_ev);
+  if (h->side) (void)hipStreamDestroy(h->side);
   h->fork_ev = h->join_ev = nullptr;
   h->side = nullptr;
 }
@@ -797,7 +798,7 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
   if (e == hipSuccess) e = dispatch_apply(h->cpt, kModeMoments, false, a, nblocks, h->apply_lds, stream);
   // the block list must outlive the kernel
   const hipError_t e2 = hipStreamSynchronize(stream);
-  hipFree(dblocks);
+  (void)hipFree(dblocks);
   if (e != hipSuccess || e2 != hipSuccess)
     return fail(MA_EHIP, "ma_debug_moments: %s", hipGetErrorString(e != hipSuccess ? e : e2));
   return MA_OK;
