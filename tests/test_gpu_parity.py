@@ -220,6 +220,31 @@ def test_long_windows_up_to_the_limit(m, steps):
     full_parity(f"m={m}", 3_000, 1024, 30, m, steps, moments=False)
 
 
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_learning_rate_schedule(wd):
+    # ma_set_lr between steps (a scheduler): the step factor and the decoupled
+    # decay 1 - lr * wd follow the current lr on both sides
+    d, B, k, m = 100_003, 16384, 1000, 4
+    rng = np.random.default_rng(21)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    opt = MicroAdam(d, B, k, m, lr=1e-3, wd=wd)
+    orc = O.FullState(O.make_cfg(d, B, k, m, 4, 0.9, 0.999, 1e-8, 1e-3, wd, 42, 0))
+    th_gpu = torch.from_numpy(theta0.copy()).cuda()
+    th_cpu = theta0.copy()
+    for t in range(1, 7):
+        lr = 1e-3 * 0.6 ** (t - 1)
+        opt.set_lr(lr)
+        orc.cfg.lr = lr
+        g = gauss_grads(rng, d, t)
+        say(f"[lr schedule] step {t}: lr={lr:.3g} wd={wd}")
+        opt.step(th_gpu, to_gpu_bf16(g))
+        torch.cuda.synchronize()
+        orc.step(th_cpu, g)
+        assert_bits_equal(f"lr t={t} window", opt.window(), orc.G)
+        assert_bits_equal(f"lr t={t} codes", opt.codes_bytes(), orc.ef)
+        assert_close_f32(f"lr t={t} theta", th_gpu.cpu().numpy(), th_cpu)
+
+
 def test_run_twice_is_bitwise_deterministic():
     runs = []
     for _ in range(2):
