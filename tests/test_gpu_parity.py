@@ -220,6 +220,17 @@ def test_long_windows_up_to_the_limit(m, steps):
     full_parity(f"m={m}", 3_000, 1024, 30, m, steps, moments=False)
 
 
+@pytest.mark.parametrize("d,k,m,beta1,beta2,eps,lr", [
+    (6 * 16384 + 777, 6 * 164, 10, 0.5, 0.95, 1e-3, 1e-2),    # fused kernel
+    (4 * 16384, 4 * 164, 37, 0.8, 0.9, 1e-6, 3e-3),            # update kernel, two slot passes
+])
+def test_other_hyperparameters(d, k, m, beta1, beta2, eps, lr):
+    # the decay tables beta^r, the bias factors and eps at values other than
+    # the defaults
+    full_parity(f"hyper b1={beta1} b2={beta2} eps={eps}", d, 16384, k, m, m + 3,
+                beta1=beta1, beta2=beta2, eps=eps, lr=lr)
+
+
 @pytest.mark.parametrize("wd", [0.0, 0.1])
 def test_learning_rate_schedule(wd):
     # ma_set_lr between steps (a scheduler): the step factor and the decoupled
