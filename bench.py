@@ -81,7 +81,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the MicroAdam step needs no communication "
-              "(every block is independent); multi-GPU runs are not part of this build.", file=sys.stderr)
+              "(every block is independent); several GPUs would each own a contiguous range of blocks, "
+              "which is not implemented here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
