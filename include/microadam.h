@@ -30,9 +30,11 @@
  * return NULL).  The code and a message are kept per calling thread
  * (ma_last_error, ma_last_error_message).  Nothing here prints or aborts.
  *
- * Streams: ma_step and ma_debug_moments only enqueue work on the stream given
- * and never synchronize.  The state/accessor calls marked "synchronous" wait
- * for the whole device.  Calls on one handle must not overlap.
+ * Streams: ma_step only enqueues work on the stream given and never
+ * synchronizes.  The debug calls (ma_debug_moments, ma_debug_residual) run on
+ * the stream given and synchronize it before returning.  The state/accessor
+ * calls marked "synchronous" wait for the whole device.  Calls on one handle
+ * must not overlap.
  */
 #ifndef MICROADAM_H
 #define MICROADAM_H
@@ -183,11 +185,27 @@ int ma_write_state(ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, 
  * paragraph, bias-corrected) for nblocks chosen blocks.  blocks: host array of
  * block numbers.  mhat_out, vhat_out: device f32[nblocks * B_d]; row q holds
  * block blocks[q], its first len_j entries valid (0 where the window has no
- * entry).  Enqueued on `stream`.  MA_EINVAL before the first step or for a
- * block number out of range.
+ * entry).  Runs on `stream` and synchronizes it before returning.  MA_EINVAL
+ * before the first step or for a block number out of range.
  */
 int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *mhat_out,
                      float *vhat_out, hipStream_t stream);
+
+/*
+ * The accumulator of the first line of the step (first paragraph of the
+ * MicroAdam page), a_t = g_t + Q^-1(e_t, delta_t, Delta_t), for nblocks chosen
+ * blocks, computed from the current codes and statistics (the state the next
+ * ma_step would start from) and the given gradients, with the step's own
+ * arithmetic (fp32: f32(g) + fmaf(code, (Delta - delta)/15, delta); with
+ * MA_FLAG_NO_EF, f32(g)).  The state is not changed.  grads: device bf16[d].
+ * blocks: host array of block numbers.  a_out: device f32[nblocks * B_d]; row q
+ * holds block blocks[q], 0 past the block's end.  Runs on `stream` and
+ * synchronizes it before returning.  MA_EINVAL for a NULL pointer or a block
+ * number out of range; MA_ENOMEM if the temporary block list cannot be
+ * allocated.
+ */
+int ma_debug_residual(ma_ctx *h, const uint16_t *grads, const int64_t *blocks, int64_t nblocks,
+                      float *a_out, hipStream_t stream);
 
 /*
  * Per-kernel timing with HIP events recorded around each launch, on the stream

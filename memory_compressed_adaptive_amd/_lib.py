@@ -32,7 +32,7 @@ MA_STATE_WINDOW = 2
 EXPORTS = (
     "ma_create", "ma_step", "ma_step_bf16", "ma_adamw_step", "ma_adamw8_step", "ma_state_bytes", "ma_aux_bytes", "ma_destroy", "ma_last_error",
     "ma_last_error_message", "ma_get_step", "ma_num_blocks", "ma_set_step", "ma_set_flags",
-    "ma_set_lr", "ma_read_state", "ma_write_state", "ma_debug_moments", "ma_set_timing",
+    "ma_set_lr", "ma_read_state", "ma_write_state", "ma_debug_moments", "ma_debug_residual", "ma_set_timing",
     "ma_kernel_times", "ma_set_pipeline", "ma_get_pipeline", "ma_set_count_touched", "ma_touched_count",
 )
 
@@ -90,6 +90,8 @@ def lib():
     L.ma_write_state.argtypes = [p, C.c_int, u64, u64, p]
     L.ma_debug_moments.restype = C.c_int
     L.ma_debug_moments.argtypes = [p, p, i64, p, p, p]
+    L.ma_debug_residual.restype = C.c_int
+    L.ma_debug_residual.argtypes = [p, p, p, i64, p, p]
     L.ma_set_timing.restype = C.c_int
     L.ma_set_timing.argtypes = [p, C.c_int]
     L.ma_kernel_times.restype = C.c_int

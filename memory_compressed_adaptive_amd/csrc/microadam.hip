@@ -804,6 +804,69 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
   return MA_OK;
 }
 
+namespace {
+
+// Test hook for the first line of the step (first paragraph of the MicroAdam
+// page): the accumulator a_t = f32(g_t) + Q^-1(e_t, delta_t, Delta_t) of the
+// listed blocks, from the current codes and statistics, with the compressor's
+// arithmetic (step (Delta - delta) / 15, then one fmaf and one add).  Row q of
+// out holds block blocks[q]; positions past the block's end are 0.
+__global__ __launch_bounds__(256) void residual_kernel(const uint16_t *g, const uint8_t *codes, const float *stats,
+                                                       const int64_t *blocks, int64_t d, int32_t B, int ef,
+                                                       float *out) {
+  const int64_t j = blocks[blockIdx.x];
+  const int64_t s = j * (int64_t)B;
+  const int64_t L = (d - s) < (int64_t)B ? (d - s) : (int64_t)B;
+  float lo = 0.f, step = 0.f;
+  if (ef) {
+    lo = stats[2 * j];
+    step = (stats[2 * j + 1] - lo) / 15.0f;
+  }
+  for (int i = (int)threadIdx.x; i < B; i += (int)blockDim.x) {
+    float v = 0.f;
+    if (i < L) {
+      const int64_t gi = s + i;
+      const float gf = __uint_as_float((uint32_t)g[gi] << 16);
+      v = gf;
+      if (ef) {
+        const uint32_t code = (codes[gi >> 1] >> (4 * (int)(gi & 1))) & 15u;
+        v = gf + fmaf((float)code, step, lo);
+      }
+    }
+    out[(int64_t)blockIdx.x * B + i] = v;
+  }
+}
+
+}  // namespace
+
+int ma_debug_residual(ma_ctx *h, const uint16_t *grads, const int64_t *blocks, int64_t nblocks, float *a_out,
+                      hipStream_t stream) {
+  clear_error();
+  if (!h || !grads || !blocks || !a_out || nblocks < 0)
+    return fail(MA_EINVAL, "ma_debug_residual: null argument");
+  if (nblocks == 0) return MA_OK;
+  if (nblocks > 0x7fffffff) return fail(MA_EINVAL, "ma_debug_residual: too many blocks");
+  for (int64_t q = 0; q < nblocks; ++q)
+    if (blocks[q] < 0 || blocks[q] >= h->n_b)
+      return fail(MA_EINVAL, "ma_debug_residual: block %lld out of range", (long long)blocks[q]);
+  DeviceGuard guard(h->device);
+  int64_t *dblocks = nullptr;
+  if (hipMalloc(&dblocks, 8 * (size_t)nblocks) != hipSuccess) return fail(MA_ENOMEM, "ma_debug_residual: allocation failed");
+  hipError_t e = hipMemcpyAsync(dblocks, blocks, 8 * (size_t)nblocks, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(residual_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, grads,
+                       (const uint8_t *)h->codes, (const float *)h->stats, (const int64_t *)dblocks, h->d, h->B,
+                       (h->flags & MA_FLAG_NO_EF) ? 0 : 1, a_out);
+    e = hipGetLastError();
+  }
+  // the block list must outlive the kernel
+  const hipError_t e2 = hipStreamSynchronize(stream);
+  (void)hipFree(dblocks);
+  if (e != hipSuccess || e2 != hipSuccess)
+    return fail(MA_EHIP, "ma_debug_residual: %s", hipGetErrorString(e != hipSuccess ? e : e2));
+  return MA_OK;
+}
+
 int ma_set_timing(ma_ctx *h, int on) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_timing: null handle");

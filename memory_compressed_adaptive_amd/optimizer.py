@@ -140,6 +140,20 @@ class MicroAdam:
                                            C.c_void_p(_stream_handle(stream))))
         return mh, vh
 
+    def residual(self, grads, blocks, stream=None):
+        """The accumulator a_t = g_t + Q^-1(e_t) the next step would start
+        from, for the given blocks and gradients (bf16 or int16 bits, CUDA),
+        as a CUDA tensor of shape [len(blocks), block]; the state is not
+        changed."""
+        import torch
+        assert grads.is_cuda and grads.is_contiguous() and grads.numel() == self.d and grads.element_size() == 2
+        blocks = np.ascontiguousarray(blocks, dtype=np.int64)
+        out = torch.empty((blocks.size, self.block), dtype=torch.float32, device="cuda")
+        _L.check(_L.lib().ma_debug_residual(self._h, C.c_void_p(grads.data_ptr()), blocks.ctypes.data_as(C.c_void_p),
+                                            blocks.size, C.c_void_p(out.data_ptr()),
+                                            C.c_void_p(_stream_handle(stream))))
+        return out
+
     def set_timing(self, on: bool):
         _L.check(_L.lib().ma_set_timing(self._h, 1 if on else 0))
 

@@ -69,6 +69,8 @@ def test_null_handles_are_safe():
     assert lib.ma_read_state(None, 0, 0, 0, None) == L.MA_EINVAL
     assert lib.ma_kernel_times(None, None, None, 0) == L.MA_EINVAL
     assert lib.ma_set_pipeline(None, 4) == L.MA_EINVAL
+    assert lib.ma_debug_residual(None, None, None, 0, None, None) == L.MA_EINVAL
+    assert lib.ma_debug_moments(None, None, 0, None, None, None) == L.MA_EINVAL
     assert lib.ma_get_pipeline(None) == -1
 
 

@@ -256,6 +256,56 @@ def test_learning_rate_schedule(wd):
         assert_close_f32(f"lr t={t} theta", th_gpu.cpu().numpy(), th_cpu)
 
 
+@pytest.mark.parametrize("B,flags,gq", [
+    (16384, 0, False),                  # per-block (delta, Delta), state from the fused kernel
+    (1003, 0, False),                   # odd B_d: code bytes straddle blocks
+    (16384, 0, True),                   # global quantizer: the one pair in every block's statistics
+    (4096, L.MA_FLAG_NO_EF, False),     # no error feedback: a = f32(g)
+])
+def test_residual_stage_a1(B, flags, gq):
+    # the first line of the step on its own: a_t = g_t + Q^-1(e_t, delta_t,
+    # Delta_t) from the state after 3 steps, against the oracle's pieces
+    d, m = 50_001, 4
+    k = d // 100
+    rng = np.random.default_rng(31)
+    opt = MicroAdam(d, B, k, m)
+    opt.set_flags(flags | (L.MA_FLAG_GLOBAL_QUANT if gq else 0))
+    no_ef = bool(flags & L.MA_FLAG_NO_EF)
+    cfg = O.make_cfg(d, B, k, m, 4, 0.9, 0.999, 1e-8, 1e-4, 0.0, 42,
+                     (O.FLAG_NO_EF if no_ef else 0) | (O.FLAG_GLOBAL_QUANT if gq else 0))
+    orc = O.FullState(cfg)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    th_gpu = torch.from_numpy(theta0.copy()).cuda()
+    th_cpu = theta0.copy()
+    for t in range(1, 4):
+        g = gauss_grads(rng, d, t)
+        opt.step(th_gpu, to_gpu_bf16(g))
+        orc.step(th_cpu, g)
+    torch.cuda.synchronize()
+    assert_bits_equal("a1 state codes", opt.codes_bytes(), orc.ef)
+    g4 = gauss_grads(rng, d, 4)
+    nb = opt.num_blocks
+    blocks = sorted({0, nb // 2, nb - 1})
+    say(f"[residual a1] B={B} flags={flags} global={gq} blocks={blocks}")
+    got = opt.residual(to_gpu_bf16(g4), blocks).cpu().numpy()
+    for q, j in enumerate(blocks):
+        s, n = O.block_range(cfg, j)
+        gf = O.bf16_to_f32(g4[s:s + n])
+        if no_ef:
+            want = gf
+        else:
+            lo, hi = (orc.stats[0], orc.stats[1]) if gq else (orc.stats[2 * j], orc.stats[2 * j + 1])
+            want = gf + O.dequant_group(O.unpack_nibbles(orc.ef, n, s), lo, hi)
+        assert want.dtype == np.float32
+        assert_bits_equal(f"a1 block {j}", got[q, :n], want)
+        assert (got[q, n:] == 0).all()
+    # the state is unchanged: the next step still matches the oracle
+    opt.step(th_gpu, to_gpu_bf16(g4))
+    orc.step(th_cpu, g4)
+    torch.cuda.synchronize()
+    assert_bits_equal("a1 then step, window", opt.window(), orc.G)
+
+
 def test_run_twice_is_bitwise_deterministic():
     runs = []
     for _ in range(2):
