@@ -282,23 +282,51 @@ void launch_global_pass(const CompressArgs &a, int64_t n_b, int64_t n_full, hipS
 }
 
 template <int CPT, bool AL>
-hipError_t launch_global_q(const CompressArgs &a, int64_t n_b, int64_t n_full, hipStream_t s) {
+void launch_global_p1(const CompressArgs &a, int64_t n_b, int64_t n_full, hipStream_t s) {
   launch_global_pass<CPT, AL, kQGlobal1>(a, n_b, n_full, s);
   hipLaunchKernelGGL(global_minmax_kernel, dim3(1), dim3(kThreads), 0, s, (const float *)a.blkmm, n_b,
                      (float *)a.gmm);
-  launch_global_pass<CPT, AL, kQGlobal2>(a, n_b, n_full, s);
+}
+
+
+// Pass 1 and the global min / max over all blocks; pass 2 for blocks
+// [b0, b1) (no deferral there: pass 1 recorded every block's cut).
+hipError_t dispatch_global_p1(int cpt, bool aligned, const CompressArgs &a, int64_t n_b, int64_t n_full,
+                              hipStream_t s) {
+  switch (cpt) {
+    case 1: aligned ? launch_global_p1<1, true>(a, n_b, n_full, s) : launch_global_p1<1, false>(a, n_b, n_full, s); break;
+    case 2: aligned ? launch_global_p1<2, true>(a, n_b, n_full, s) : launch_global_p1<2, false>(a, n_b, n_full, s); break;
+    case 4: aligned ? launch_global_p1<4, true>(a, n_b, n_full, s) : launch_global_p1<4, false>(a, n_b, n_full, s); break;
+    default: aligned ? launch_global_p1<8, true>(a, n_b, 0, s) : launch_global_p1<8, false>(a, n_b, 0, s); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t dispatch_global_q(int cpt, bool aligned, const CompressArgs &a, int64_t n_b, int64_t n_full,
-                             hipStream_t s) {
+template <int CPT, bool AL>
+hipError_t launch_global_p2(const CompressArgs &a, int64_t b0, int64_t b1, int64_t n_full, hipStream_t s) {
+  const int64_t f1 = std::min(b1, n_full);
+  if (CPT <= 4 && AL && f1 > b0) {
+    constexpr int C4 = CPT <= 4 ? CPT : 4;
+    hipLaunchKernelGGL((compress_full_kernel<C4, true, kQGlobal2>), dim3((unsigned)(f1 - b0)), dim3(kThreads), 0, s,
+                       a, b0);
+  }
+  const int64_t g0 = std::max(b0, (CPT <= 4 && AL) ? n_full : (int64_t)0);
+  if (b1 > g0)
+    hipLaunchKernelGGL((compress_kernel<CPT, AL, true, kQGlobal2>), dim3((unsigned)(b1 - g0)), dim3(kThreads), 0, s,
+                       a, g0);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_global_p2(int cpt, bool aligned, const CompressArgs &a, int64_t b0, int64_t b1, int64_t n_full,
+                              hipStream_t s) {
   switch (cpt) {
-    case 1: return aligned ? launch_global_q<1, true>(a, n_b, n_full, s) : launch_global_q<1, false>(a, n_b, n_full, s);
-    case 2: return aligned ? launch_global_q<2, true>(a, n_b, n_full, s) : launch_global_q<2, false>(a, n_b, n_full, s);
-    case 4: return aligned ? launch_global_q<4, true>(a, n_b, n_full, s) : launch_global_q<4, false>(a, n_b, n_full, s);
-    default: return aligned ? launch_global_q<8, true>(a, n_b, 0, s) : launch_global_q<8, false>(a, n_b, 0, s);
+    case 1: return aligned ? launch_global_p2<1, true>(a, b0, b1, n_full, s) : launch_global_p2<1, false>(a, b0, b1, n_full, s);
+    case 2: return aligned ? launch_global_p2<2, true>(a, b0, b1, n_full, s) : launch_global_p2<2, false>(a, b0, b1, n_full, s);
+    case 4: return aligned ? launch_global_p2<4, true>(a, b0, b1, n_full, s) : launch_global_p2<4, false>(a, b0, b1, n_full, s);
+    default: return aligned ? launch_global_p2<8, true>(a, b0, b1, 0, s) : launch_global_p2<8, false>(a, b0, b1, 0, s);
   }
 }
+
 
 ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float decay) {
   ApplyArgs a{};
@@ -538,28 +566,47 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   const bool ef = !(h->flags & MA_FLAG_NO_EF);
   hipError_t e = hipSuccess;
 
-  // Global quantizer: the compressor in two passes around a global min / max,
-  // then the update; all on the caller's stream.
+  // Global quantizer: the compressor's first pass (selection, window row,
+  // each block's min / max and cut) and the global min / max over all blocks;
+  // then the second pass (codes and statistics) on the caller's stream and,
+  // concurrently on the side stream, the update, which reads only the window
+  // and the parameters: neither writes what the other reads.
   if (ef && (h->flags & MA_FLAG_GLOBAL_QUANT)) {
     ca.blkmm = h->blkmm;
     ca.selinfo = h->selinfo;
     ca.gmm = h->gmm;
-    hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr;
+    hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr, t4 = nullptr, t5 = nullptr;
     if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h)) || !(t2 = timing_event(h)) ||
-                      !(t3 = timing_event(h))))
+                      !(t3 = timing_event(h)) || !(t4 = timing_event(h)) || !(t5 = timing_event(h))))
       return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (!ensure_pipeline(h, 1)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
     ca.deferred = h->deferred;
     ca.n_deferred = h->n_deferred;
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
     if (t0) (void)hipEventRecord(t0, stream);
-    e = dispatch_global_q(h->cpt, g_al, ca, h->n_b, n_full, stream);
+    e = dispatch_global_p1(h->cpt, g_al, ca, h->n_b, n_full, stream);
     if (t1) (void)hipEventRecord(t1, stream);
-    if (t2) (void)hipEventRecord(t2, stream);
-    if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream, bf);
-    if (t3) {
-      (void)hipEventRecord(t3, stream);
+    if (e == hipSuccess) e = hipEventRecord(h->fork_ev, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
+    if (e == hipSuccess) {
+      if (t4) (void)hipEventRecord(t4, h->side);
+      e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, h->side, bf);
+      if (t5) (void)hipEventRecord(t5, h->side);
+    }
+    if (e == hipSuccess) {
+      if (t2) (void)hipEventRecord(t2, stream);
+      e = dispatch_global_p2(h->cpt, g_al, ca, 0, h->n_b, n_full, stream);
+      if (t3) (void)hipEventRecord(t3, stream);
+    }
+    {
+      hipError_t e2 = hipEventRecord(h->join_ev, h->side);
+      if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, h->join_ev, 0);
+      if (e == hipSuccess) e = e2;
+    }
+    if (t0) {
       h->events.push_back({0, t0, t1});
-      h->events.push_back({1, t2, t3});
+      h->events.push_back({0, t2, t3});
+      h->events.push_back({1, t4, t5});
     }
     if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
     h->t = t;
