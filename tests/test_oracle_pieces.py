@@ -94,7 +94,8 @@ def test_xi16_keys_on_seed_step_block_and_element():
 # ------------------------------------------------------------------ blocks and quotas
 
 CONFIG_D = {
-    # flat parameter counts of the five synthetic workloads (tensor lists in the design doc)
+    # flat parameter counts of the five synthetic workloads: the weight matrices of each
+    # architecture (attention 4·h², MLP 2 or 3 matrices, embeddings), biases and norms left out
     "tiny": 2**20,
     "bert_base": 12 * (4 * 768 * 768 + 2 * 768 * 3072) + 30522 * 768,
     "opt_1_3b": 24 * (4 * 2048 * 2048 + 2 * 2048 * 8192) + 50272 * 2048,
