@@ -42,15 +42,18 @@ def kernel_source_sha():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(workload: str, m: int):
+def load_traffic(workload: str, m: int, variant: bool, kernels):
     """Counter-measured HBM bytes per launch, if a committed summary exists for
-    the current kernel source (null once the kernels have changed)."""
+    the current kernel source (null once the kernels have changed).  The
+    summaries are of the default step (fp32 parameters, per-block quantizer,
+    sparse update, no decay): a variant run, or one whose kernels are not the
+    ones the summary measured, gets none."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_m{m}.json")
-    if not os.path.exists(path):
+    if variant or not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("kernel_source_sha256") != kernel_source_sha() or set(t.get("kernels", {})) != set(kernels):
         return None
     return t
 
@@ -223,7 +226,7 @@ def main():
     bytes_launch = kern[dom] / launches[dom]
     ms_launch = kt[dom][0] / kt[dom][1]
     achieved = bytes_launch / (ms_launch * 1e-3) / 1e9
-    traffic = load_traffic(w.name, m)
+    traffic = load_traffic(w.name, m, bool(args.dense or args.global_quant or args.bf16_params or args.wd), kern)
     traffic_bytes = None
     if traffic is not None and dom in traffic.get("kernels", {}):
         kt_ = traffic["kernels"][dom]
