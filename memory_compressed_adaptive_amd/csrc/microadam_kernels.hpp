@@ -1174,8 +1174,10 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
             if (r < 0) r += M;
             const float f1 = decay_factor(sm.beta, r), f2 = decay_factor(sm.beta, M + r);
             if (slv[u] < n) {
-              s_z1[slv[u]] = s_z1[slv[u]] + f1 * vv[u];
-              s_z2[slv[u]] = s_z2[slv[u]] + f2 * (vv[u] * vv[u]);
+              // both read before either is written: one LDS round trip, not two
+              const float a1 = s_z1[slv[u]], a2 = s_z2[slv[u]];
+              s_z1[slv[u]] = a1 + f1 * vv[u];
+              s_z2[slv[u]] = a2 + f2 * (vv[u] * vv[u]);
             }
             __syncthreads();
           }
@@ -1193,8 +1195,9 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         const float V = bf16_bits_to_f32(e >> 16);
         const uint32_t sl = s_wbase[I >> 5] + (uint32_t)__popc(s_bits[I >> 5] & ((1u << (I & 31u)) - 1u)) - s0;
         if (sl < n) {
-          s_z1[sl] = s_z1[sl] + f1 * V;
-          s_z2[sl] = s_z2[sl] + f2 * (V * V);
+          const float a1 = s_z1[sl], a2 = s_z2[sl];
+          s_z1[sl] = a1 + f1 * V;
+          s_z2[sl] = a2 + f2 * (V * V);
         }
       }
       __syncthreads();
