@@ -12,7 +12,7 @@ from memory_compressed_adaptive_amd import MicroAdam
 from memory_compressed_adaptive_amd import _lib as L
 from memory_compressed_adaptive_amd import synth
 
-from gpu_harness import (assert_bits_equal, assert_close_f32, full_parity, gauss_grads,
+from gpu_harness import (assert_bits_equal, assert_close_f32, full_parity, full_state_parity, gauss_grads,
                          sampled_parity, say, to_gpu_bf16)
 
 pytestmark = pytest.mark.gpu
@@ -397,6 +397,15 @@ def test_create_destroy_does_not_leak():
 
 def test_bert_base_sampled():
     sampled_parity("bert_base", synth.WORKLOADS["bert_base"], 10, 4, every=97)
+
+
+def test_bert_base_full_state():
+    # every block, past the window's first wrap (m = 10, 12 steps)
+    full_state_parity("bert_base full", synth.WORKLOADS["bert_base"], 10, 12)
+
+
+def test_opt_1_3b_full_state():
+    full_state_parity("opt_1_3b full", synth.WORKLOADS["opt_1_3b"], 10, 3)
 
 
 def test_opt_1_3b_sampled():

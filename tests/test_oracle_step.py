@@ -213,6 +213,30 @@ def test_block_state_equals_full_state():
             np.testing.assert_array_equal(bs.stats, full.stats[2 * j: 2 * j + 2])
 
 
+def test_threaded_full_step_equals_single_threaded():
+    # the full-size GPU parity tests step the oracle with its blocks spread over
+    # threads; that must be the single-threaded full step exactly, every array
+    # bitwise, ragged last block included
+    from oracle_threads import oracle_step_threaded
+    rng = np.random.default_rng(31)
+    d, B, m = 300_001 - 1, 4096, 4     # 74 blocks, the last of 1004 elements
+    cfg = O.make_cfg(d, B, d // 100, m)
+    full = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    th2 = theta.copy()
+    ef2 = np.zeros_like(full.ef)
+    st2 = np.zeros_like(full.stats)
+    G2 = np.zeros_like(full.G)
+    for t in range(1, 7):
+        g = _grads(rng, d)
+        full.step(theta, g)
+        oracle_step_threaded(cfg, t, th2, g, ef2, st2, G2, threads=5)
+        np.testing.assert_array_equal(th2.view(np.uint32), theta.view(np.uint32))
+        np.testing.assert_array_equal(ef2, full.ef)
+        np.testing.assert_array_equal(st2.view(np.uint32), full.stats.view(np.uint32))
+        np.testing.assert_array_equal(G2, full.G)
+
+
 def test_odd_block_length_nibbles_straddle():
     # B odd: blocks share EF bytes; per-element nibble order must still hold
     rng = np.random.default_rng(28)
