@@ -118,3 +118,10 @@ def check(rc: int):
         code, msg = last_error()
         raise MicroAdamError(rc, msg)
     return rc
+
+
+def require(ok: bool, what: str) -> None:
+    """An argument check of the binding, raised as ValueError (unlike an
+    assert it also holds under python -O)."""
+    if not ok:
+        raise ValueError(what)

@@ -62,10 +62,12 @@ class MicroAdam:
     def step(self, params, grads, stream=None):
         """params: fp32 (4-byte elements) or bfloat16 (2-byte elements, updated
         through ma_step_bf16)."""
-        assert params.is_cuda and grads.is_cuda
-        assert params.numel() == self.d and grads.numel() == self.d
-        assert params.is_contiguous() and grads.is_contiguous()
-        assert params.element_size() in (2, 4) and grads.element_size() == 2
+        _L.require(params.is_cuda and grads.is_cuda, "params and grads must be CUDA tensors")
+        _L.require(params.numel() == self.d and grads.numel() == self.d,
+                   f"params and grads must have d = {self.d} elements")
+        _L.require(params.is_contiguous() and grads.is_contiguous(), "params and grads must be contiguous")
+        _L.require(params.element_size() in (2, 4) and grads.element_size() == 2,
+                   "params must be fp32 or bf16 and grads bf16 (or int16 bits)")
         fn = _L.lib().ma_step if params.element_size() == 4 else _L.lib().ma_step_bf16
         _L.check(fn(self._h, C.c_void_p(params.data_ptr()), C.c_void_p(grads.data_ptr()),
                     C.c_void_p(_stream_handle(stream))))
@@ -146,7 +148,8 @@ class MicroAdam:
         as a CUDA tensor of shape [len(blocks), block]; the state is not
         changed."""
         import torch
-        assert grads.is_cuda and grads.is_contiguous() and grads.numel() == self.d and grads.element_size() == 2
+        _L.require(grads.is_cuda and grads.is_contiguous() and grads.numel() == self.d and grads.element_size() == 2,
+                   f"grads must be a contiguous bf16 CUDA tensor of d = {self.d} elements")
         blocks = np.ascontiguousarray(blocks, dtype=np.int64)
         out = torch.empty((blocks.size, self.block), dtype=torch.float32, device="cuda")
         _L.check(_L.lib().ma_debug_residual(self._h, C.c_void_p(grads.data_ptr()), blocks.ctypes.data_as(C.c_void_p),

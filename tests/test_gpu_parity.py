@@ -377,6 +377,12 @@ def test_error_codes_on_gpu_handle():
     assert lib.ma_read_state(opt.handle, L.MA_STATE_CODES, 0, 10_000, C.c_void_p(1)) == L.MA_EINVAL
     buf = (C.c_uint8 * 8)()
     assert lib.ma_debug_moments(opt.handle, buf, 1, C.c_void_p(1), C.c_void_p(1), None) == L.MA_EINVAL
+    # the binding rejects what the C ABI could not check (host memory, lengths,
+    # element sizes) before any call
+    for p_, g_ in ((theta.cpu(), g), (theta, g[:999]), (theta, g.float()), (theta.double(), g)):
+        with pytest.raises(ValueError):
+            opt.step(p_, g_)
+    assert opt.t == 0
     opt.step(theta, g)
     torch.cuda.synchronize()
     assert opt.t == 1
