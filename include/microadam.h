@@ -95,7 +95,10 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
  * in place.  grads: caller-owned device bf16[d] (raw bits), read only.  Both
  * must be element-aligned and live on the handle's device.  Enqueued on
  * `stream`, asynchronous.  Returns MA_OK, MA_EINVAL (null/misaligned pointer)
- * or MA_EHIP (launch error); t advances only on success.
+ * or MA_EHIP (launch error); t advances only on success.  After MA_EHIP some
+ * of the step's kernels may already be enqueued, so the state can be partly
+ * advanced: restore a saved state (ma_write_state, ma_set_step) or destroy
+ * the handle.
  */
 int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream);
 

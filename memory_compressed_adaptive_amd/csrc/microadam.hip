@@ -149,6 +149,19 @@ hipEvent_t timing_event(ma_ctx *h) {
   return hipEventCreate(&e) == hipSuccess ? e : nullptr;
 }
 
+// Takes n timing events, all or none: on failure the ones taken go back to
+// the pool.  A step takes its events before it launches anything.
+bool take_events(ma_ctx *h, hipEvent_t *ev, int n) {
+  for (int i = 0; i < n; ++i) {
+    ev[i] = timing_event(h);
+    if (!ev[i]) {
+      for (int q = 0; q < i; ++q) h->pool.push_back(ev[q]);
+      return false;
+    }
+  }
+  return true;
+}
+
 int64_t floor_mul_div(int64_t k, int64_t x, int64_t d) {
   const unsigned __int128 p = (unsigned __int128)(uint64_t)k * (uint64_t)x;
   return (int64_t)(p / (uint64_t)d);
@@ -575,11 +588,10 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     ca.blkmm = h->blkmm;
     ca.selinfo = h->selinfo;
     ca.gmm = h->gmm;
-    hipEvent_t t0 = nullptr, t1 = nullptr, t2 = nullptr, t3 = nullptr, t4 = nullptr, t5 = nullptr;
-    if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h)) || !(t2 = timing_event(h)) ||
-                      !(t3 = timing_event(h)) || !(t4 = timing_event(h)) || !(t5 = timing_event(h))))
-      return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     if (!ensure_pipeline(h, 1)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
+    hipEvent_t tg[6] = {};
+    if (h->timing && !take_events(h, tg, 6)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    hipEvent_t t0 = tg[0], t1 = tg[1], t2 = tg[2], t3 = tg[3], t4 = tg[4], t5 = tg[5];
     ca.deferred = h->deferred;
     ca.n_deferred = h->n_deferred;
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
@@ -620,11 +632,11 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   if (h->fused_ok && n_full > 0 && mode == kModeSparse && !(h->flags & MA_FLAG_UNFUSED)) {
     ca.deferred = h->deferred;
     ca.n_deferred = h->n_deferred;
+    hipEvent_t tf[2] = {};
+    if (h->timing && !take_events(h, tf, 2)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    hipEvent_t t0 = tf[0], t1 = tf[1];
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
     e = hipGetLastError();
-    hipEvent_t t0 = nullptr, t1 = nullptr;
-    if (h->timing && (!(t0 = timing_event(h)) || !(t1 = timing_event(h))))
-      return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     if (t0) (void)hipEventRecord(t0, stream);
     if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, ca, aa, n_full, h->apply_lds, stream, bf);
     if (t1) {
@@ -646,6 +658,9 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
 
   const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
   if (chunks > 1 && !ensure_pipeline(h, chunks)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
+  // per range: compress start / end, update start / end
+  std::vector<hipEvent_t> tp(h->timing ? 4 * (size_t)chunks : 0, nullptr);
+  if (!tp.empty() && !take_events(h, tp.data(), (int)tp.size())) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
   hipStream_t upd = chunks > 1 ? h->side : stream;
   if (chunks > 1) {
     e = hipEventRecord(h->fork_ev, stream);
@@ -661,14 +676,13 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     CompressArgs cai = ca;
     cai.deferred = h->deferred + b0;
     cai.n_deferred = h->n_deferred + i;
-    hipEvent_t t0 = nullptr, t1 = nullptr;
-    if (h->timing && !(t0 = timing_event(h)) ) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
-    if (h->timing && !(t1 = timing_event(h)) ) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    hipEvent_t t0 = tp.empty() ? nullptr : tp[4 * (size_t)i], t1 = tp.empty() ? nullptr : tp[4 * (size_t)i + 1];
     if (t0) (void)hipEventRecord(t0, stream);
     e = dispatch_compress(h->cpt, g_al, ef, cai, b0, b1, n_full, stream);
     if (t1) {
       (void)hipEventRecord(t1, stream);
       h->events.push_back({0, t0, t1});
+      tp[4 * (size_t)i] = tp[4 * (size_t)i + 1] = nullptr;
     }
     if (e != hipSuccess) break;
     if (chunks > 1) {
@@ -678,16 +692,18 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     }
     ApplyArgs aai = aa;
     aai.first_block = b0;
-    hipEvent_t u0 = nullptr, u1 = nullptr;
-    if (h->timing && !(u0 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
-    if (h->timing && !(u1 = timing_event(h))) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    hipEvent_t u0 = tp.empty() ? nullptr : tp[4 * (size_t)i + 2], u1 = tp.empty() ? nullptr : tp[4 * (size_t)i + 3];
     if (u0) (void)hipEventRecord(u0, upd);
     e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, h->apply_lds, upd, bf);
     if (u1) {
       (void)hipEventRecord(u1, upd);
       h->events.push_back({1, u0, u1});
+      tp[4 * (size_t)i + 2] = tp[4 * (size_t)i + 3] = nullptr;
     }
   }
+  // events of ranges a failed launch left unused go back to the pool
+  for (hipEvent_t ev : tp)
+    if (ev) h->pool.push_back(ev);
   if (chunks > 1) {
     hipError_t e2 = hipEventRecord(h->join_ev, h->side);
     if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, h->join_ev, 0);
@@ -832,6 +848,7 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
     return fail(MA_EINVAL, "ma_debug_moments: null argument");
   if (h->t < 1) return fail(MA_EINVAL, "ma_debug_moments: no step has run yet");
   if (nblocks == 0) return MA_OK;
+  if (nblocks > 0x7fffffff) return fail(MA_EINVAL, "ma_debug_moments: too many blocks");
   for (int64_t q = 0; q < nblocks; ++q)
     if (blocks[q] < 0 || blocks[q] >= h->n_b) return fail(MA_EINVAL, "ma_debug_moments: block %lld out of range", (long long)blocks[q]);
   DeviceGuard guard(h->device);
