@@ -205,6 +205,11 @@ def main():
     bytes_c = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb       # g, codes r+w, window row, stats r+w
     if args.global_quant:
         bytes_c += 2 * d + (d + 1) // 2 + 16 * nb                # second pass: g and codes again, cut
+    # global quantizer: the first pass reads g and the codes and writes the
+    # window row and each block's min / max and cut; the second reads g and
+    # the codes again and writes the codes and statistics
+    bytes_c1 = 2 * d + (d + 1) // 2 + 4 * k + 16 * nb
+    bytes_c2 = bytes_c - bytes_c1
     pb = 2 if args.bf16_params else 4                            # bytes per parameter
     if args.wd:
         bytes_a = 4 * m * k + 2 * pb * d                        # window read, every parameter r+w
@@ -212,7 +217,13 @@ def main():
         bytes_a = 4 * m * k + 2 * pb * touched                  # window read, touched parameters r+w
     # Full blocks run as one fused kernel (compress + update per block) when
     # the library takes that path; the kernels then share the bytes by blocks.
-    if kt["step_fused"][1] > 0:
+    if kt["step_fused"][1] > 0 and args.global_quant:
+        # the first pass fused with the update; the second pass alone
+        n_full = d // B
+        f = n_full / nb
+        kern = {"step_fused": f * (bytes_c1 + bytes_a), "compress": bytes_c2 + (1 - f) * bytes_c1,
+                "adamstats_apply": (1 - f) * bytes_a}
+    elif kt["step_fused"][1] > 0:
         n_full = d // B
         f = n_full / nb
         kern = {"step_fused": f * (bytes_c + bytes_a), "compress": (1 - f) * bytes_c,

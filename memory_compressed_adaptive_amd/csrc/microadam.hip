@@ -246,12 +246,14 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
 }
 
 // The fused step for blocks [0, n_full): the fused kernel, then the blocks it
-// deferred (compress, then update, from the device list).
-template <int CPT, bool EF, bool BF>
+// deferred (compress, then update, from the device list).  QMODE kQGlobal1:
+// the global quantizer's first pass in place of the compressor.
+template <int CPT, bool EF, bool BF, int QMODE = kQBlock>
 hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a, (int64_t)0);
+  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a,
+                     (int64_t)0);
   const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
-  hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF>), dim3(grid2), dim3(kThreads), 0, s, c);
+  hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF, QMODE>), dim3(grid2), dim3(kThreads), 0, s, c);
   ApplyArgs al = a;
   al.blocks = c.deferred;
   al.n_list = c.n_deferred;
@@ -313,6 +315,38 @@ hipError_t dispatch_global_p1(int cpt, bool aligned, const CompressArgs &a, int6
     default: aligned ? launch_global_p1<8, true>(a, n_b, 0, s) : launch_global_p1<8, false>(a, n_b, 0, s); break;
   }
   return hipGetLastError();
+}
+
+// The global quantizer's first pass fused with the update: blocks [0, n_full)
+// by the fused kernel (and its deferred blocks), the rest (a partial last
+// block) by pass 1 and then the update; then the global min / max over all
+// blocks.  The second pass follows on the same stream.
+template <int CPT, bool BF>
+hipError_t launch_fused_global1(const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al, int64_t n_b,
+                                int64_t n_full, size_t apply_lds, hipStream_t s) {
+  hipError_t e = launch_fused<CPT, true, BF, kQGlobal1>(c, a, n_full, apply_lds, s);
+  if (e == hipSuccess && n_b > n_full) {
+    hipLaunchKernelGGL((compress_kernel<CPT, true, true, kQGlobal1>), dim3((unsigned)(n_b - n_full)), dim3(kThreads), 0,
+                       s, c, n_full);
+    ApplyArgs at = a;
+    at.first_block = n_full;
+    e = dispatch_apply(CPT, mode, p_al, at, n_b - n_full, apply_lds, s, BF);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(global_minmax_kernel, dim3(1), dim3(kThreads), 0, s, (const float *)c.blkmm, n_b, (float *)c.gmm);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_fused_global1(int cpt, bool bf, const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al,
+                                  int64_t n_b, int64_t n_full, size_t apply_lds, hipStream_t s) {
+  switch (cpt) {
+    case 1: return bf ? launch_fused_global1<1, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                      : launch_fused_global1<1, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+    case 2: return bf ? launch_fused_global1<2, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                      : launch_fused_global1<2, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+    default: return bf ? launch_fused_global1<4, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                       : launch_fused_global1<4, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+  }
 }
 
 template <int CPT, bool AL>
@@ -595,6 +629,30 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     ca.deferred = h->deferred;
     ca.n_deferred = h->n_deferred;
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
+    // Full blocks: the first pass fused with the update (the update needs only
+    // the block's window, which the first pass completes), then the second
+    // pass alone.  Neither writes what the other reads.
+    if (h->fused_ok && n_full > 0 && mode == kModeSparse && !(h->flags & MA_FLAG_UNFUSED)) {
+      if (t0) (void)hipEventRecord(t0, stream);
+      e = dispatch_fused_global1(h->cpt, bf, ca, aa, mode, p_al, h->n_b, n_full, h->apply_lds, stream);
+      if (t1) (void)hipEventRecord(t1, stream);
+      if (e == hipSuccess) {
+        if (t2) (void)hipEventRecord(t2, stream);
+        e = dispatch_global_p2(h->cpt, g_al, ca, 0, h->n_b, n_full, stream);
+        if (t3) (void)hipEventRecord(t3, stream);
+      }
+      if (t0) {
+        h->events.push_back({2, t0, t1});
+        h->events.push_back({0, t2, t3});
+        h->pool.push_back(t4);
+        h->pool.push_back(t5);
+      }
+      if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
+      h->t = t;
+      h->last_c1 = c1;
+      h->last_c2 = c2;
+      return MA_OK;
+    }
     if (t0) (void)hipEventRecord(t0, stream);
     e = dispatch_global_p1(h->cpt, g_al, ca, h->n_b, n_full, stream);
     if (t1) (void)hipEventRecord(t1, stream);

@@ -1348,10 +1348,13 @@ constexpr int kFusedEnt = 1984;
 // LDS beside its global copy.  Co-resident workgroups are in different
 // phases, so the VALU-bound compressor and the memory-bound update share each
 // CU.  A block the compressor defers is left entirely (compress and update)
-// to compress_deferred_kernel and apply_list_kernel.
-template <int CPT, bool EF, bool BF = false>
+// to compress_deferred_kernel and apply_list_kernel.  QMODE kQGlobal1: the
+// global quantizer's first pass (selection, window row, the block's min / max
+// and cut) with the update; the codes are left to the second pass.
+template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(CompressArgs C, ApplyArgs A,
                                                                              int64_t first_block) {
+  static_assert(QMODE == kQBlock || (QMODE == kQGlobal1 && EF), "the fused kernel runs a step or a first pass");
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   __shared__ uint32_t ent[kFusedEnt];
@@ -1392,7 +1395,7 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   fbits.es = es;
   fbits.M = A.m;
   fbits.tm = A.tm;
-  const bool done = compress_block<CPT, true, true, EF, true>(C, sm, j, j * (int64_t)C.B, CPT * kChunkSpan, in.off,
+  const bool done = compress_block<CPT, true, true, EF, true, QMODE>(C, sm, j, j * (int64_t)C.B, CPT * kChunkSpan, in.off,
                                                               in.kb, &st, &in, &ent[A.tm * es], st_words, &fbits);
   if (!done) return;
   __syncthreads();

@@ -132,23 +132,28 @@ def test_fused_step_with_deferred_blocks():
     full_parity("fused deferred", 6 * 16384, 16384, 6 * 164, 5, 6, grad_fn=mixed)
 
 
-@pytest.mark.parametrize("d,B,k,m,misalign", [
-    (100_003, 16384, 1000, 4, False),   # full blocks and a ragged last block
-    (50_001, 8192, 2000, 3, True),      # unaligned gradients, odd d
-    (7, 3, 2, 2, False),                # every block partial
+@pytest.mark.parametrize("d,B,k,m,misalign,unfused", [
+    (100_003, 16384, 1000, 4, False, False),   # full blocks (first pass fused with the update), ragged last block
+    (100_003, 16384, 1000, 4, False, True),    # the same, first pass and update as separate kernels
+    (3 * 8192, 8192, 600, 2, False, False),    # fused, two chunks per thread, no partial block
+    (50_001, 8192, 2000, 3, True, False),      # unaligned gradients, odd d
+    (7, 3, 2, 2, False, False),                # every block partial
 ])
-def test_global_quantizer(d, B, k, m, misalign):
+def test_global_quantizer(d, B, k, m, misalign, unfused):
     # one (delta, Delta) over all d: pass 1, global min / max, pass 2
-    full_parity(f"global Q d={d} B={B}", d, B, k, m, 6, misalign=misalign, global_quant=True)
+    full_parity(f"global Q d={d} B={B} unfused={unfused}", d, B, k, m, 6, misalign=misalign, global_quant=True,
+                gpu_only_flags=L.MA_FLAG_UNFUSED if unfused else 0)
 
 
-def test_global_quantizer_with_deferred_blocks():
+@pytest.mark.parametrize("unfused", [False, True])
+def test_global_quantizer_with_deferred_blocks(unfused):
     # tie-heavy blocks leave the staged first pass for the general selection
     def mixed(rng, d, t):
         g = gauss_grads(rng, d, t)
         g[16384:3 * 16384] = O.bf16_rne(np.full(2 * 16384, 1e-3, np.float32))
         return g
-    full_parity("global Q deferred", 6 * 16384, 16384, 6 * 164, 4, 5, grad_fn=mixed, global_quant=True)
+    full_parity(f"global Q deferred unfused={unfused}", 6 * 16384, 16384, 6 * 164, 4, 5, grad_fn=mixed,
+                global_quant=True, gpu_only_flags=L.MA_FLAG_UNFUSED if unfused else 0)
 
 
 def test_global_quantizer_single_block_equals_block_mode():
