@@ -248,22 +248,32 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
 // The fused step for blocks [0, n_full): the fused kernel, then the blocks it
 // deferred (compress, then update, from the device list).  QMODE kQGlobal1:
 // the global quantizer's first pass in place of the compressor.
-template <int CPT, bool EF, bool BF, int QMODE = kQBlock>
+template <int CPT, bool EF, bool BF, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
 hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE>), dim3((unsigned)n_full), dim3(kThreads), 0, s, c, a,
-                     (int64_t)0);
+  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0, s,
+                     c, a, (int64_t)0);
   const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
   hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF, QMODE>), dim3(grid2), dim3(kThreads), 0, s, c);
   ApplyArgs al = a;
   al.blocks = c.deferred;
   al.n_list = c.n_deferred;
-  hipLaunchKernelGGL((apply_list_kernel<CPT, BF>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
+  hipLaunchKernelGGL((apply_list_kernel<CPT, BF, MODE>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
   return hipGetLastError();
 }
 
 template <bool BF>
-hipError_t dispatch_fused_t(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
+hipError_t dispatch_fused_t(int cpt, bool ef, bool dense, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
                             size_t apply_lds, hipStream_t s) {
+  if (dense) {   // decoupled decay: every parameter streamed (aligned parameters only)
+    switch (cpt) {
+      case 1: return ef ? launch_fused<1, true, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s)
+                        : launch_fused<1, false, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s);
+      case 2: return ef ? launch_fused<2, true, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s)
+                        : launch_fused<2, false, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s);
+      default: return ef ? launch_fused<4, true, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s)
+                         : launch_fused<4, false, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s);
+    }
+  }
   switch (cpt) {
     case 1: return ef ? launch_fused<1, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<1, false, BF>(c, a, n_full, apply_lds, s);
     case 2: return ef ? launch_fused<2, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<2, false, BF>(c, a, n_full, apply_lds, s);
@@ -271,10 +281,10 @@ hipError_t dispatch_fused_t(int cpt, bool ef, const CompressArgs &c, const Apply
   }
 }
 
-hipError_t dispatch_fused(int cpt, bool ef, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
+hipError_t dispatch_fused(int cpt, bool ef, bool dense, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
                           size_t apply_lds, hipStream_t s, bool bf) {
-  return bf ? dispatch_fused_t<true>(cpt, ef, c, a, n_full, apply_lds, s)
-            : dispatch_fused_t<false>(cpt, ef, c, a, n_full, apply_lds, s);
+  return bf ? dispatch_fused_t<true>(cpt, ef, dense, c, a, n_full, apply_lds, s)
+            : dispatch_fused_t<false>(cpt, ef, dense, c, a, n_full, apply_lds, s);
 }
 
 // The global quantizer's launches over all blocks: pass 1 (full aligned
@@ -686,8 +696,9 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   }
 
   // Fused path: every full block runs compress and update in one workgroup;
-  // a partial last block (if any) runs the two kernels after it.
-  if (h->fused_ok && n_full > 0 && mode == kModeSparse && !(h->flags & MA_FLAG_UNFUSED)) {
+  // a partial last block (if any) runs the two kernels after it.  The dense
+  // update (decoupled decay) is fused for 16-byte aligned parameters.
+  if (h->fused_ok && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
     ca.deferred = h->deferred;
     ca.n_deferred = h->n_deferred;
     hipEvent_t tf[2] = {};
@@ -696,7 +707,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
     e = hipGetLastError();
     if (t0) (void)hipEventRecord(t0, stream);
-    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, ca, aa, n_full, h->apply_lds, stream, bf);
+    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, mode == kModeDense, ca, aa, n_full, h->apply_lds, stream, bf);
     if (t1) {
       (void)hipEventRecord(t1, stream);
       h->events.push_back({2, t0, t1});

@@ -1321,15 +1321,16 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(ApplyArgs A) {
   apply_block<CPT, MODE, ALIGNED, false, BF>(A, j, (int64_t)blockIdx.x, apply_smem<CPT>(A, smem, s_cnt, j));
 }
 
-// The sparse update of the blocks in the device list A.blocks[0 .. *A.n_list).
-template <int CPT, bool BF = false>
+// The update (MODE 0 or 1) of the blocks in the device list
+// A.blocks[0 .. *A.n_list).
+template <int CPT, bool BF = false, int MODE = kModeSparse>
 __global__ __launch_bounds__(kThreads) void apply_list_kernel(ApplyArgs A) {
   extern __shared__ uint32_t smem[];
   __shared__ uint32_t s_cnt[kWaves + 1];
   const unsigned int n = *A.n_list;
   for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
     const int64_t j = A.blocks[q];
-    apply_block<CPT, kModeSparse, false, false, BF>(A, j, 0, apply_smem<CPT>(A, smem, s_cnt, j));
+    apply_block<CPT, MODE, false, false, BF>(A, j, 0, apply_smem<CPT>(A, smem, s_cnt, j));
     __syncthreads();
   }
 }
@@ -1350,11 +1351,14 @@ constexpr int kFusedEnt = 1984;
 // CU.  A block the compressor defers is left entirely (compress and update)
 // to compress_deferred_kernel and apply_list_kernel.  QMODE kQGlobal1: the
 // global quantizer's first pass (selection, window row, the block's min / max
-// and cut) with the update; the codes are left to the second pass.
-template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock>
+// and cut) with the update; the codes are left to the second pass.  MODE:
+// the update's mode (kModeDense with decoupled decay), PAL: 16-byte aligned
+// parameters (required by the dense mode here).
+template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(CompressArgs C, ApplyArgs A,
                                                                              int64_t first_block) {
   static_assert(QMODE == kQBlock || (QMODE == kQGlobal1 && EF), "the fused kernel runs a step or a first pass");
+  static_assert(MODE == kModeSparse || (MODE == kModeDense && PAL), "dense updates in the fused kernel are aligned");
   __shared__ CompressSmem<CPT> sm;
   __shared__ FullBlockStage<CPT> st;
   __shared__ uint32_t ent[kFusedEnt];
@@ -1414,7 +1418,7 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   as.beta = s_beta;
   as.off = in.off;
   as.kb = in.kb;
-  apply_block<CPT, kModeSparse, false, true, BF>(A, j, 0, as);
+  apply_block<CPT, MODE, PAL, true, BF>(A, j, 0, as);
 }
 
 }  // namespace microadam

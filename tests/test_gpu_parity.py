@@ -132,6 +132,23 @@ def test_fused_step_with_deferred_blocks():
     full_parity("fused deferred", 6 * 16384, 16384, 6 * 164, 5, 6, grad_fn=mixed)
 
 
+@pytest.mark.parametrize("B", [4096, 8192, 16384])
+def test_fused_step_with_decay(B):
+    # decoupled decay: the fused kernel streams every parameter of its block
+    # (dense update), the ragged last block runs the two kernels after it
+    d = 31 * B + 1234
+    full_parity(f"fused decay B={B}", d, B, d // 100, 10, 12, lr=1e-2, wd=0.1)
+
+
+def test_fused_decay_with_deferred_blocks():
+    # tie-heavy blocks deferred by the fused kernel get the dense update from the list kernel
+    def mixed(rng, d, t):
+        g = gauss_grads(rng, d, t)
+        g[16384:3 * 16384] = O.bf16_rne(np.full(2 * 16384, 1e-3, np.float32))
+        return g
+    full_parity("fused decay deferred", 6 * 16384, 16384, 6 * 164, 5, 6, lr=1e-2, wd=0.1, grad_fn=mixed)
+
+
 @pytest.mark.parametrize("d,B,k,m,misalign,unfused", [
     (100_003, 16384, 1000, 4, False, False),   # full blocks (first pass fused with the update), ragged last block
     (100_003, 16384, 1000, 4, False, True),    # the same, first pass and update as separate kernels
