@@ -1117,34 +1117,42 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
     const bool decay_pass = (MODE == kModeDense) && s0 == 0 && A.decay != 1.0f;
     float th[CPT][kChunk];
     uint32_t tb[CPT];
-    if (MODE == kModeDense) {
+    // (fp32 parameters in the fused kernel: the dense loads wait until after
+    // the row sums, the block's parameters would otherwise stay in registers
+    // across them; measured faster for fp32 and slower for bf16, whose
+    // parameters take half the registers)
+    constexpr bool kLateTheta = MODE == kModeDense && PRELOADED && !BF;
+    auto load_theta = [&]() {
+      if (MODE == kModeDense) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int i0 = c * kChunkSpan + tid * kChunk;
-        tb[c] = (i0 < L) ? (s_bits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
-        tb[c] |= tb[c] ? 0x100u : 0u;   // bit 8: the thread's 8 parameters are streamed
-        if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
-          if (ALIGNED && BF && i0 + kChunk <= L) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(A.theta16 + s + i0);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        for (int c = 0; c < CPT; ++c) {
+          const int i0 = c * kChunkSpan + tid * kChunk;
+          tb[c] = (i0 < L) ? (s_bits[i0 >> 5] >> (i0 & 31)) & 0xffu : 0u;
+          tb[c] |= tb[c] ? 0x100u : 0u;   // bit 8: the thread's 8 parameters are streamed
+          if ((tb[c] >> 8) || (decay_pass && i0 < L)) {
+            if (ALIGNED && BF && i0 + kChunk <= L) {
+              const u32x4 w = *reinterpret_cast<const u32x4 *>(A.theta16 + s + i0);
+              const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e)
-              th[c][e] = (e & 1) ? u2f(ww[e >> 1] & 0xffff0000u) : u2f(ww[e >> 1] << 16);
-          } else if (ALIGNED && i0 + kChunk <= L) {
-            const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
-            const float4 v1 = *reinterpret_cast<const float4 *>(A.theta + s + i0 + 4);
-            th[c][0] = v0.x; th[c][1] = v0.y; th[c][2] = v0.z; th[c][3] = v0.w;
-            th[c][4] = v1.x; th[c][5] = v1.y; th[c][6] = v1.z; th[c][7] = v1.w;
+              for (int e = 0; e < kChunk; ++e)
+                th[c][e] = (e & 1) ? u2f(ww[e >> 1] & 0xffff0000u) : u2f(ww[e >> 1] << 16);
+            } else if (ALIGNED && i0 + kChunk <= L) {
+              const float4 v0 = *reinterpret_cast<const float4 *>(A.theta + s + i0);
+              const float4 v1 = *reinterpret_cast<const float4 *>(A.theta + s + i0 + 4);
+              th[c][0] = v0.x; th[c][1] = v0.y; th[c][2] = v0.z; th[c][3] = v0.w;
+              th[c][4] = v1.x; th[c][5] = v1.y; th[c][6] = v1.z; th[c][7] = v1.w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? ld_param<BF>(A, s + i0 + e) : 0.f;
+            }
           } else {
 #pragma unroll
-            for (int e = 0; e < kChunk; ++e) th[c][e] = (i0 + e < L) ? ld_param<BF>(A, s + i0 + e) : 0.f;
+            for (int e = 0; e < kChunk; ++e) th[c][e] = 0.f;
           }
-        } else {
-#pragma unroll
-          for (int e = 0; e < kChunk; ++e) th[c][e] = 0.f;
         }
       }
-    }
+    };
+    if (!kLateTheta) load_theta();
     // AdamStats: z[I] += beta^r V, rows in physical order, one row at a time.
     // Entries in LDS with at most one per thread and row: the thread's
     // entries of 8 rows at a time are looked up (slot, V) before the rows are
@@ -1202,6 +1210,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
       }
       __syncthreads();
     }
+    if (kLateTheta) load_theta();
     // m_hat = c1 z1, v_hat = c2 z2; theta -= lr * m_hat / (sqrt(v_hat) + eps)
     if (MODE == kModeSparse) {
 #pragma unroll
