@@ -331,10 +331,10 @@ hipError_t dispatch_global_p1(int cpt, bool aligned, const CompressArgs &a, int6
 // by the fused kernel (and its deferred blocks), the rest (a partial last
 // block) by pass 1 and then the update; then the global min / max over all
 // blocks.  The second pass follows on the same stream.
-template <int CPT, bool BF>
+template <int CPT, bool BF, int MODE, bool PAL>
 hipError_t launch_fused_global1(const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al, int64_t n_b,
                                 int64_t n_full, size_t apply_lds, hipStream_t s) {
-  hipError_t e = launch_fused<CPT, true, BF, kQGlobal1>(c, a, n_full, apply_lds, s);
+  hipError_t e = launch_fused<CPT, true, BF, kQGlobal1, MODE, PAL>(c, a, n_full, apply_lds, s);
   if (e == hipSuccess && n_b > n_full) {
     hipLaunchKernelGGL((compress_kernel<CPT, true, true, kQGlobal1>), dim3((unsigned)(n_b - n_full)), dim3(kThreads), 0,
                        s, c, n_full);
@@ -347,16 +347,25 @@ hipError_t launch_fused_global1(const CompressArgs &c, const ApplyArgs &a, int m
   return hipGetLastError();
 }
 
+template <int MODE, bool PAL>
+hipError_t dispatch_fused_global1_t(int cpt, bool bf, const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al,
+                                    int64_t n_b, int64_t n_full, size_t apply_lds, hipStream_t s) {
+  switch (cpt) {
+    case 1: return bf ? launch_fused_global1<1, true, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                      : launch_fused_global1<1, false, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+    case 2: return bf ? launch_fused_global1<2, true, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                      : launch_fused_global1<2, false, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+    default: return bf ? launch_fused_global1<4, true, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                       : launch_fused_global1<4, false, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
+  }
+}
+
+// mode kModeDense requires 16-byte aligned parameters (p_al)
 hipError_t dispatch_fused_global1(int cpt, bool bf, const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al,
                                   int64_t n_b, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  switch (cpt) {
-    case 1: return bf ? launch_fused_global1<1, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
-                      : launch_fused_global1<1, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
-    case 2: return bf ? launch_fused_global1<2, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
-                      : launch_fused_global1<2, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
-    default: return bf ? launch_fused_global1<4, true>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
-                       : launch_fused_global1<4, false>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
-  }
+  return mode == kModeDense
+             ? dispatch_fused_global1_t<kModeDense, true>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s)
+             : dispatch_fused_global1_t<kModeSparse, false>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s);
 }
 
 template <int CPT, bool AL>
@@ -641,8 +650,9 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
     // Full blocks: the first pass fused with the update (the update needs only
     // the block's window, which the first pass completes), then the second
-    // pass alone.  Neither writes what the other reads.
-    if (h->fused_ok && n_full > 0 && mode == kModeSparse && !(h->flags & MA_FLAG_UNFUSED)) {
+    // pass alone.  Neither writes what the other reads.  The dense update
+    // (decoupled decay) is fused for 16-byte aligned parameters.
+    if (h->fused_ok && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
       if (t0) (void)hipEventRecord(t0, stream);
       e = dispatch_fused_global1(h->cpt, bf, ca, aa, mode, p_al, h->n_b, n_full, h->apply_lds, stream);
       if (t1) (void)hipEventRecord(t1, stream);

@@ -162,6 +162,13 @@ def test_global_quantizer(d, B, k, m, misalign, unfused):
                 gpu_only_flags=L.MA_FLAG_UNFUSED if unfused else 0)
 
 
+@pytest.mark.parametrize("unfused,misalign", [(False, False), (True, False), (False, True)])
+def test_global_quantizer_with_decay(unfused, misalign):
+    # decoupled decay: the dense update after (or fused with) the first pass
+    full_parity(f"global Q decay unfused={unfused} misalign={misalign}", 100_003, 16384, 1000, 4, 5, lr=1e-2, wd=0.1,
+                misalign=misalign, global_quant=True, gpu_only_flags=L.MA_FLAG_UNFUSED if unfused else 0)
+
+
 @pytest.mark.parametrize("unfused", [False, True])
 def test_global_quantizer_with_deferred_blocks(unfused):
     # tie-heavy blocks leave the staged first pass for the general selection
