@@ -140,6 +140,11 @@ def test_fused_step_with_decay(B):
     full_parity(f"fused decay B={B}", d, B, d // 100, 10, 12, lr=1e-2, wd=0.1)
 
 
+def test_fused_decay_without_error_feedback():
+    # the fused kernel's dense update with the error feedback switched off
+    full_parity("fused decay no EF", 5 * 16384 + 77, 16384, 900, 6, 8, lr=1e-2, wd=0.1, flags=O.FLAG_NO_EF)
+
+
 def test_fused_decay_with_deferred_blocks():
     # tie-heavy blocks deferred by the fused kernel get the dense update from the list kernel
     def mixed(rng, d, t):
@@ -205,6 +210,7 @@ def test_global_quantizer_single_block_equals_block_mode():
     (70_000, 16384, 700, 4, 0.1, 0, True),                     # decay, parameters 2 bytes off
     (20_011, 1003, 500, 3, 0.0, 0, False),                     # odd B_d
     (100_003, 16384, 1000, 4, 0.0, L.MA_FLAG_GLOBAL_QUANT, False),  # one (delta, Delta) over all d
+    (100_003, 16384, 1000, 4, 0.1, L.MA_FLAG_GLOBAL_QUANT, False),  # the same with decay (dense, fused)
     (60_000, 16384, 6000, 37, 0.0, 0, False),                  # window too large for LDS: rows from HBM
 ])
 def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
