@@ -313,3 +313,107 @@ def test_state_bytes_and_memory_paragraph():
         c = O.make_cfg(13015449600, 16384, 13015449600 // 100, mm)
         assert (O.state_bytes(c) < 2 * 13015449600) == below
     assert 1 - m * k / d >= page["min_update_sparsity_at_m10"] - 1e-9
+
+
+# ---------------------------------------------------------------- error feedback carried across steps
+
+def _compose_step(cfg, t, g, ef_prev, stats_prev, global_q, mistake=None, stats_new=None):
+    """Step t's compressor outputs (window row, statistics, unpacked codes),
+    composed from separately pinned pieces (the bf16 widening, dequantizer,
+    Top-k, bf16 rounding, min / max and quantizer) in the order of the first
+    paragraph: a_t = g_t + Q^-1(e_t, delta_t, Delta_t); (I_t, V_t) = T_k(|a_t|);
+    zero those entries; e_{t+1} = Q(a_t, delta_{t+1}, Delta_{t+1}).  `mistake`
+    plants one plausible error, for the guard test below."""
+    d = cfg.d
+    nb = O.num_blocks(cfg)
+    gf = O.bf16_to_f32(g)
+    a = np.empty(d, np.float32)
+    row = np.zeros(cfg.k, np.uint32)
+    for j in range(nb):
+        s, n = O.block_range(cfg, j)
+        codes = O.unpack_nibbles(ef_prev, n, s)
+        jj = (j + 1) % nb if mistake == "neighbour stats" else j
+        src = stats_new if mistake == "new stats" else stats_prev
+        lo, hi = (src[0], src[1]) if global_q else (src[2 * jj], src[2 * jj + 1])
+        xh = O.dequant_group(codes, lo, hi)
+        if mistake == "dropped feedback":
+            a[s:s + n] = gf[s:s + n]
+        elif mistake == "sign":
+            a[s:s + n] = gf[s:s + n] - xh
+        else:
+            a[s:s + n] = gf[s:s + n] + xh
+        off, kb = O.block_quota(cfg, j)
+        sel = O.topk(a[s:s + n], kb)
+        vb = O.bf16_rne(a[s + sel]).astype(np.uint32)
+        row[off:off + kb] = sel.astype(np.uint32) | (vb << 16)
+    resid = a.copy()
+    for j in range(nb):
+        s, n = O.block_range(cfg, j)
+        off, kb = O.block_quota(cfg, j)
+        sel = (row[off:off + kb] & 0xffff).astype(np.int64)
+        if mistake != "quantize before zeroing":
+            resid[s + sel] = 0.0
+    tq = t - 1 if mistake == "stale step in the generator" else t
+    codes_new = np.empty(d, np.uint8)
+    if global_q:
+        lo, hi = O.group_minmax(resid)
+        stats = np.array([lo, hi], np.float32)
+    else:
+        stats = np.empty(2 * nb, np.float32)
+    for j in range(nb):
+        s, n = O.block_range(cfg, j)
+        if not global_q:
+            lo, hi = O.group_minmax(resid[s:s + n])
+            stats[2 * j], stats[2 * j + 1] = lo, hi
+        codes_new[s:s + n] = O.quant_group(resid[s:s + n], cfg.seed, tq, j, 0, lo, hi)
+    return row, stats, codes_new
+
+
+def _carry_over_run(global_q):
+    rng = np.random.default_rng(41 + global_q)
+    d, B, m = 50_001, 4096, 3            # 13 blocks, the last of 841 elements
+    cfg = O.make_cfg(d, B, d // 100, m, flags=O.FLAG_GLOBAL_QUANT if global_q else 0)
+    st = O.FullState(cfg)
+    theta = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    out = []
+    for t in range(1, 5):
+        g = _grads(rng, d)
+        ef_prev, stats_prev = st.ef.copy(), st.stats.copy()
+        st.step(theta, g)
+        out.append((t, g, ef_prev, stats_prev, st.G.reshape(m, -1)[t % m].copy(), st.stats.copy(),
+                    O.unpack_nibbles(st.ef, d)))
+    return cfg, out
+
+
+@pytest.mark.parametrize("global_q", [False, True])
+def test_error_feedback_carries_over_steps(global_q):
+    """Steps 2-4 (where e_t != 0) from the previous step's codes and statistics:
+    the window row, the new statistics and the new codes all equal the
+    composition of the pinned pieces."""
+    cfg, out = _carry_over_run(global_q)
+    for t, g, ef_prev, stats_prev, row, stats, codes in out:
+        if t >= 2:
+            assert np.any(ef_prev != 0)         # the feedback is really there
+        r, s, c = _compose_step(cfg, t, g, ef_prev, stats_prev, global_q)
+        np.testing.assert_array_equal(row, r, err_msg=f"window row, t={t}")
+        np.testing.assert_array_equal(stats.view(np.uint32), s.view(np.uint32), err_msg=f"statistics, t={t}")
+        np.testing.assert_array_equal(codes, c, err_msg=f"codes, t={t}")
+
+
+@pytest.mark.parametrize("global_q", [False, True])
+@pytest.mark.parametrize("mistake", ["new stats", "sign", "dropped feedback", "neighbour stats",
+                                     "quantize before zeroing", "stale step in the generator"])
+def test_error_feedback_mistakes_would_be_caught(global_q, mistake):
+    # guard for the pin above: each planted mistake changes at least one of the
+    # compared outputs on the same inputs at some step t >= 2, so an oracle
+    # making it would fail the pin
+    if mistake == "neighbour stats" and global_q:
+        pytest.skip("one pair over all d: there is no neighbouring block's pair")
+    cfg, out = _carry_over_run(global_q)
+    caught = False
+    for t, g, ef_prev, stats_prev, row, stats, codes in out[1:]:
+        r, s, c = _compose_step(cfg, t, g, ef_prev, stats_prev, global_q, mistake, stats_new=stats)
+        if not (np.array_equal(row, r) and np.array_equal(stats.view(np.uint32), s.view(np.uint32))
+                and np.array_equal(codes, c)):
+            caught = True
+    assert caught, mistake
