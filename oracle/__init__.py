@@ -65,6 +65,7 @@ def lib():
     L.orc_topk.argtypes = [p, i64, i64, p]
     L.orc_quant_group.argtypes = [p, i64, u64, i64, i64, i64, f32, f32, p]
     L.orc_group_minmax.argtypes = [p, i64, p, p]
+    L.orc_range_reset.argtypes = [p, p]
     L.orc_dequant_group.argtypes = [p, i64, f32, f32, p]
     L.orc_block_step.restype = C.c_int
     L.orc_block_step.argtypes = [cfgp, i64, i64, p, p, p, i64, p, p, i64, p, p]

@@ -184,8 +184,9 @@ static int cmp_int32(const void *pa, const void *pb)
 }
 
 /* T_k(|a|): the page ranks by magnitude.  Reading: the key is the fp32 |a| taken
- * as its 31-bit pattern (monotone in |a| for finite values), larger first, and
- * equal keys go to the lower position.  Written as a full sort, then the first
+ * as its 31-bit pattern (monotone in |a| for finite values; +-Inf above every
+ * finite value and NaN above that), larger first, and equal keys go to the
+ * lower position.  Written as a full sort, then the first
  * kb positions re-sorted ascending (the order window entries are stored in). */
 void orc_topk(const float *a, int64_t n, int64_t kb, int32_t *sel_out)
 {
@@ -249,13 +250,37 @@ void orc_quant_group(const float *x, int64_t n, uint64_t seed, int64_t t, int64_
     }
     for (int64_t i = 0; i < n; ++i) {
         float y = (x[i] - lo) * inv;
+        /* The step only passes finite values in [lo, hi] (it drops non-finite
+         * residual entries and resets a group whose range is not finite), so
+         * y lies in [0, 15] up to rounding.  Outside that, no float-to-int
+         * conversion is left undefined: y >= 15 gives 15 (as the cap below
+         * would), y < 0 or NaN gives 0. */
+        if (!(y >= 0.0f)) {
+            codes_out[i] = 0;
+            continue;
+        }
+        if (y >= 15.0f) {
+            codes_out[i] = 15;
+            continue;
+        }
         float f = floorf(y);
         float frac = y - f;
         uint32_t u = orc_xi16(seed, t, j, local0 + i);
         int code = (int)f + (((float)u < frac * 65536.0f) ? 1 : 0);
         if (code > 15) code = 15;
-        if (code < 0) code = 0;
         codes_out[i] = (uint8_t)code;
+    }
+}
+
+/* Reading for a residual whose range Delta - delta is not a finite fp32 value
+ * (values of both signs near the fp32 limit): the levels would be infinitely
+ * far apart and the dequantizer would produce NaN, so the group's error
+ * feedback is reset: delta = Delta = 0, hence every code 0. */
+void orc_range_reset(float *lo, float *hi)
+{
+    if (!(*hi - *lo <= FLT_MAX)) {
+        *lo = 0.0f;
+        *hi = 0.0f;
     }
 }
 
@@ -301,6 +326,12 @@ static void block_compress(const orc_cfg *c, int64_t t, int64_t j,
         free(codes);
         free(xh);
     }
+    /* Reading for non-finite values (the page assumes finite gradients): a NaN
+     * of the accumulator stands for the canonical quiet NaN, whatever payload
+     * or sign the arithmetic left on it, so its Top-k key is 0x7fc00000 and
+     * its window value the bfloat16 0x7fc0. */
+    for (int64_t i = 0; i < len; ++i)
+        if (isnan(a_out[i])) a_out[i] = u2f(0x7fc00000u);
 
     /* (I_t, V_t) = T_k(|a_t|); V is the signed a rounded to bfloat16 */
     int64_t row = t % c->m;
@@ -317,6 +348,11 @@ static void block_compress(const orc_cfg *c, int64_t t, int64_t j,
         for (int64_t q = 0; q < kb; ++q) a_out[sel[q]] = 0.0f;
         free(sel);
     }
+    /* Reading: the keys of NaN and +-Inf are above every finite key, so they
+     * are selected first; any left over (more than kb in the block) are
+     * dropped from the error feedback, which stays finite. */
+    for (int64_t i = 0; i < len; ++i)
+        if (!isfinite(a_out[i])) a_out[i] = 0.0f;
 }
 
 /* Steps 6-7 of a block: AdamStats over the window, then the AdamW update. */
@@ -379,6 +415,7 @@ int orc_block_step(const orc_cfg *c, int64_t t, int64_t j,
         float lo, hi;
         uint8_t *codes = (uint8_t *)malloc((size_t)len);
         orc_group_minmax(a, len, &lo, &hi);
+        orc_range_reset(&lo, &hi);
         orc_quant_group(a, len, c->seed, t, j, 0, lo, hi, codes);
         for (int64_t i = 0; i < len; ++i) orc_set_nibble(ef, nib0 + i, codes[i]);
         stats[0] = lo;
@@ -418,6 +455,7 @@ int orc_step(const orc_cfg *c, int64_t t, float *theta, const uint16_t *g,
     if (!(c->flags & ORC_FLAG_NO_EF)) {
         float lo, hi;
         orc_group_minmax(a, c->d, &lo, &hi);
+        orc_range_reset(&lo, &hi);
         uint8_t *codes = (uint8_t *)malloc((size_t)c->B);
         for (int64_t j = 0; j < nb; ++j) {
             int64_t s, len;

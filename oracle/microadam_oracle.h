@@ -68,6 +68,8 @@ void     orc_topk(const float *a, int64_t n, int64_t kb, int32_t *sel_out);
 void     orc_quant_group(const float *x, int64_t n, uint64_t seed, int64_t t, int64_t j,
                          int64_t local0, float lo, float hi, uint8_t *codes_out);
 void     orc_group_minmax(const float *x, int64_t n, float *lo, float *hi);
+/* a range hi - lo that is not finite resets the pair to (0, 0) */
+void     orc_range_reset(float *lo, float *hi);
 void     orc_dequant_group(const uint8_t *codes, int64_t n, float lo, float hi, float *out);
 
 /* nibble access: element i of a packed array lives in byte i/2, low nibble for even i */
