@@ -250,6 +250,8 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
 // the global quantizer's first pass in place of the compressor.
 template <int CPT, bool EF, bool BF, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
 hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
+  // the kernel's LDS holds at most kFusedBeta decay factors (2m)
+  if (2 * (int64_t)a.m > kFusedBeta) return hipErrorInvalidValue;
   hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0, s,
                      c, a, (int64_t)0);
   const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
@@ -482,9 +484,12 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
   h->apply_lds = 8 * (size_t)W + 8 * (size_t)m + 4 * (size_t)h->ent_cap + 10 * (size_t)h->cap;
   // expected fraction of positions present in a full window: 1 - (1 - k/d)^m
   h->dense_default = false;   // measured: gathering touched parameters wins at m = 1 and m = 10
-  // fused kernel: full 4096-element chunks, CPT <= 4, and the m window rows
-  // (padded to 64 entries each) within kFusedEnt entries of LDS
-  h->fused_ok = h->cpt <= 4 && B_d == h->cpt * kChunkSpan && (int64_t)m * ((kb_max + 63) & ~63LL) <= kFusedEnt;
+  // fused kernel: full 4096-element chunks, CPT <= 4, the m window rows
+  // (padded to 64 entries each) within kFusedEnt entries of LDS, and the 2m
+  // decay factors within its kFusedBeta (checked on its own: with k = 0 the
+  // rows take no space at any m)
+  h->fused_ok = h->cpt <= 4 && B_d == h->cpt * kChunkSpan && (int64_t)m * ((kb_max + 63) & ~63LL) <= kFusedEnt &&
+                2 * (int64_t)m <= kFusedBeta;
   h->chunks = h->n_b >= 8192 ? 8 : 1;
 
   h->codes_bytes = (size_t)((d + 1) / 2);

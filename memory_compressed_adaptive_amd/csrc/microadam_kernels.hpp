@@ -1,20 +1,25 @@
 // HIP kernels of the MicroAdam step for CDNA4 (gfx950).
 //
 // The step is the one on the page "MicroAdam (Sparse-Gradient Adaptive
-// Optimization with Quantized Error Feedback)", first paragraph.  Its five
-// stages run as two kernels, each launched with one 512-thread workgroup
-// (8 wave64s) per B_d-block:
+// Optimization with Quantized Error Feedback)", first paragraph.  Its stages
+// are two phases of work per B_d-block, each run by one 512-thread workgroup
+// (8 wave64s):
 //
-//   compress_kernel  = ef_dequant_accumulate + block_topk + zeroing +
-//                      ef_requant + ring_write.  The block's accumulator a_t
-//                      lives only in registers (8 consecutive elements per
-//                      thread per 4096-element chunk); g and the 4-bit codes
-//                      are read once and the codes written once.
-//   apply_kernel     = adamstats_apply.  The m window segments of the block are
-//                      turned into a bitmap of touched positions, each touched
-//                      position gets a compact LDS slot, the rows are summed
-//                      into the slots in row order (a barrier per row), and
-//                      only the touched parameters are read and written.
+//   compress  = ef_dequant_accumulate + block_topk + zeroing + ef_requant +
+//               ring_write.  The block's accumulator a_t lives only in
+//               registers (8 consecutive elements per thread per 4096-element
+//               chunk); g and the 4-bit codes are read once and the codes
+//               written once.
+//   apply     = adamstats_apply.  The m window segments of the block are
+//               turned into a bitmap of touched positions, each touched
+//               position gets a compact LDS slot, the rows are summed into the
+//               slots in row order, and only the touched parameters are read
+//               and written.
+//
+// step_full_kernel runs both phases of a block in one workgroup (the default
+// for full, aligned blocks whose window fits its LDS); compress_full_kernel /
+// compress_kernel and apply_kernel run them as two kernels (a partial last
+// block, long windows, unaligned inputs).
 //
 // Bit-exactness with the CPU oracle rests on: fp32 with one rounding per
 // operation (built with -ffp-contract=off), the explicit fmaf of the
@@ -92,6 +97,22 @@ __device__ __forceinline__ uint32_t pcg_hash(uint32_t x) {
   return (w >> 22u) ^ w;
 }
 
+// Top-k keys.  The key of a value is the 31-bit pattern of |x|: for finite
+// values that is the order of |x|, +-Inf is above every finite value and NaN
+// above that.  Every NaN takes the key of the canonical quiet NaN, so neither
+// the selection nor the window depends on the payload or sign a NaN carries.
+constexpr uint32_t kKeyInf = 0x7f800000u;
+constexpr uint32_t kKeyNaN = 0x7fc00000u;
+__device__ __forceinline__ uint32_t topk_key(float x) {
+  const uint32_t k = f2u(x) & 0x7fffffffu;
+  return k > kKeyInf ? kKeyNaN : k;
+}
+// The window value of a selected element (its fp32 bits and key): bfloat16,
+// round to nearest even; a NaN is stored as the canonical 0x7fc0.
+__device__ __forceinline__ uint32_t window_bf16(uint32_t bits, uint32_t key) {
+  return key == kKeyNaN ? 0x7fc0u : f32_to_bf16_rne(u2f(bits));
+}
+
 // ------------------------------------------------------------------ wave and block helpers
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63u); }
@@ -142,6 +163,24 @@ __device__ __forceinline__ float wave_minmax(float v) {
 }
 __device__ __forceinline__ float wave_min(float v) { return wave_minmax<false>(v); }
 __device__ __forceinline__ float wave_max(float v) { return wave_minmax<true>(v); }
+
+// the same over unsigned integers (Top-k keys, NaN keys included)
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+#define MA_STEP(CTRL, RM)                                                            \
+  {                                                                                 \
+    const uint32_t o = dpp_u32<CTRL, RM>(v, v);                                     \
+    v = MAX ? max(v, o) : min(v, o);                                                \
+  }
+  MA_STEP(0x121, 0xf)
+  MA_STEP(0x122, 0xf)
+  MA_STEP(0x124, 0xf)
+  MA_STEP(0x128, 0xf)
+  MA_STEP(0x142, 0xa)
+  MA_STEP(0x143, 0xc)
+#undef MA_STEP
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 
 // Sum over the workgroup (two barriers; s_red holds kWaves words).
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *s_red) {
@@ -393,13 +432,14 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   }
 #define MA_VALID(i) (FULL || (i) < L)
 
-  // ---------------- block_topk: the k_b largest |a| (keys = 31-bit patterns),
-  // ties to the lower index.  For finite values the key order is the order of
-  // |a| as floats, so the passes over all elements compare |a| (a free source
-  // modifier) with thresholds given as keys; the inputs must be finite.  Result: threshold key T and idx_last, the index
-  // of the last selected element with key T; an element is selected iff
-  // key > T, or key == T and index <= idx_last.  exact: every element with key
-  // T is selected (then "key >= T" alone decides).
+  // ---------------- block_topk: the k_b largest keys (topk_key: the 31-bit
+  // pattern of |a|, NaN canonical), ties to the lower index.  For finite
+  // thresholds the key order is the order of |a| as floats, so the passes over
+  // all elements compare |a| (a free source modifier), written so that a NaN
+  // compares above every finite threshold.  Result: threshold key T and
+  // idx_last, the index of the last selected element with key T; an element is
+  // selected iff key > T, or key == T and index <= idx_last.  exact: every
+  // element with key T is selected (then "key >= T" alone decides).
   uint32_t T = 0x7f800000u;   // k_b = 0: the key of +inf, above every finite |a|
   int idx_last = -1;
   bool exact = true;
@@ -417,7 +457,8 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       // at least kWaves * q >= k_b distinct elements reach it.
       // For finite values the 31-bit key order is the order of |a| as floats,
       // so the streaming passes compare |a| (a free source modifier) instead of
-      // materialising keys.
+      // materialising keys.  The lane maxima skip NaN (fmaxf), so tau is
+      // reached by real elements; every NaN is a candidate below.
       float lanemax_f = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c)
@@ -440,27 +481,31 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       // cleared (ordered before the selection by the barriers below)
       if (fb)
         for (int w = tid; w < CPT * kChunkSpan / 32; w += kThreads) fb->bits[w] = 0u;
-      // (2) gather the candidates (key >= tau) into LDS in index order
+      // (2) gather the candidates (key >= tau: !(|a| < tau), which NaN
+      // passes) into LDS in index order
       uint32_t cnt[CPT], pos[CPT], C;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         uint32_t n = 0;
 #pragma unroll
         for (int e = 0; e < kChunk; ++e)
-          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) >= tau_f) ? 1u : 0u;
+          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && !(fabsf(a[c][e]) < tau_f)) ? 1u : 0u;
         cnt[c] = n;
       }
       ordered_offsets<CPT>(cnt, pos, C, sm.cnt);
       if (C <= (uint32_t)kCandMax) {
+        // the counting pass's test, recomputed rather than kept (32 lane
+        // masks held across the scan would spill): against a copy of tau the
+        // compiler cannot see through
+        float tau_g = tau_f;
+        asm volatile("" : "+v"(tau_g));
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
           uint32_t p = pos[c];
 #pragma unroll
           for (int e = 0; e < kChunk; ++e) {
             const int i = c * kChunkSpan + tid * kChunk + e;
-            // written as !(x < tau) so it is recomputed rather than kept
-            // from the counting pass (the same test for finite values)
-            const bool cd = MA_VALID(i) && !(fabsf(a[c][e]) < tau_f);
+            const bool cd = MA_VALID(i) && !(fabsf(a[c][e]) < tau_g);
             if (cd) sm.cand[p] = make_uint2(f2u(a[c][e]), (uint32_t)i);
             p += cd ? 1u : 0u;
           }
@@ -478,10 +523,10 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
           for (int r = 0; r < kCandMax / 64; ++r) {
             const int ci = r * 64 + lane;
-            ck[r] = (r < R && ci < (int)C) ? (sm.cand[ci].x & 0x7fffffffu) : 0u;
+            ck[r] = (r < R && ci < (int)C) ? topk_key(u2f(sm.cand[ci].x)) : 0u;
             kmax = max(kmax, ck[r]);
           }
-          kmax = f2u(wave_max(u2f(kmax)));   // non-negative floats order like their bits
+          kmax = wave_minmax_u32<true>(kmax);
           // T lies in [tau, kmax], so it shares their common leading bits;
           // search the rest MSB first.  Invariant: count(key >= Pk) >= k_b.
           // Padding lanes hold key 0 and never reach a candidate value >= 1.
@@ -504,8 +549,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
                 for (int r = 0; r < kCandMax / 64; ++r)
                   if (r < R && ck[r] >= cand) mn = min(mn, ck[r]);
-                Pk = (uint32_t)__builtin_amdgcn_readlane(
-                    (int)f2u(wave_min(u2f(mn == 0xffffffffu ? 0x7f800000u : mn))), 63);
+                Pk = wave_minmax_u32<false>(mn);
                 cut = true;
               }
             }
@@ -552,7 +596,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
               const bool sel = in && (ck[r] > Pk || (ck[r] == Pk && idx <= last));
               const uint64_t m = __ballot(sel);
               if (sel) {
-                const uint32_t ent = (uint32_t)idx | (f32_to_bf16_rne(u2f(sm.cand[ci].x)) << 16);
+                const uint32_t ent = (uint32_t)idx | (window_bf16(sm.cand[ci].x, ck[r]) << 16);
                 dst[wrote + (int)lanes_below(m)] = ent;
                 if (lds_row) lds_row[wrote + (int)lanes_below(m)] = ent;
                 if (fb && (ent & 0x7fff0000u)) atomicOr(&fb->bits[idx >> 5], 1u << (idx & 31));
@@ -561,9 +605,11 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
             }
           }
           if (lane == 0) {
-            sm.sel[0] = Pk;
+            // a non-finite threshold key is handed on as "every key >= +Inf's"
+            // (only non-finite values are selected, and all of them become 0)
+            sm.sel[0] = min(Pk, kKeyInf);
             sm.sel[1] = (uint32_t)last;
-            sm.sel[2] = (cut || ntie == need) ? 1u : 0u;
+            sm.sel[2] = (cut || ntie == need || Pk >= kKeyInf) ? 1u : 0u;
           }
           __builtin_amdgcn_s_setprio(0);
         } else {
@@ -599,7 +645,8 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
     }
     if (!DEFER && !done) {
       // General path (k_b > 512, k_b == L, or too many candidates): exact
-      // MSB-first bit search over the whole block with workgroup counts.
+      // MSB-first bit search over the whole block with workgroup counts, on
+      // the keys themselves (any key, NaN and +-Inf included).
       uint32_t P = 0;
       for (int b = 30; b >= 0; --b) {
         const uint32_t cand = P | (1u << b);
@@ -608,7 +655,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
         for (int c = 0; c < CPT; ++c)
 #pragma unroll
           for (int e = 0; e < kChunk; ++e)
-            n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) >= u2f(cand)) ? 1u : 0u;
+            n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && topk_key(a[c][e]) >= cand) ? 1u : 0u;
         if ((int)block_sum(n, sm.red) >= kb) P = cand;
       }
       uint32_t ngt = 0;
@@ -616,7 +663,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       for (int c = 0; c < CPT; ++c)
 #pragma unroll
         for (int e = 0; e < kChunk; ++e)
-          ngt += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) > u2f(P)) ? 1u : 0u;
+          ngt += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && topk_key(a[c][e]) > P) ? 1u : 0u;
       const int need = kb - (int)block_sum(ngt, sm.red);
       uint32_t cnt[CPT], pos[CPT], tot;
 #pragma unroll
@@ -624,7 +671,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
         uint32_t n = 0;
 #pragma unroll
         for (int e = 0; e < kChunk; ++e)
-          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && fabsf(a[c][e]) == u2f(P)) ? 1u : 0u;
+          n += (MA_VALID(c * kChunkSpan + tid * kChunk + e) && topk_key(a[c][e]) == P) ? 1u : 0u;
         cnt[c] = n;
       }
       ordered_offsets<CPT>(cnt, pos, tot, sm.cnt);
@@ -634,7 +681,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          if (MA_VALID(i) && fabsf(a[c][e]) == u2f(P)) {
+          if (MA_VALID(i) && topk_key(a[c][e]) == P) {
             if ((int)p == need - 1) sm.sel[1] = (uint32_t)i;
             ++p;
           }
@@ -651,8 +698,8 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          const float x = fabsf(a[c][e]);
-          n += (MA_VALID(i) && (x > u2f(T) || (x == u2f(T) && i <= idx_last))) ? 1u : 0u;
+          const uint32_t x = topk_key(a[c][e]);
+          n += (MA_VALID(i) && (x > T || (x == T && i <= idx_last))) ? 1u : 0u;
         }
         cnt[c] = n;
       }
@@ -664,24 +711,37 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
         for (int e = 0; e < kChunk; ++e) {
           const int i = c * kChunkSpan + tid * kChunk + e;
-          const float x = fabsf(a[c][e]);
-          if (MA_VALID(i) && (x > u2f(T) || (x == u2f(T) && i <= idx_last))) {
-            const uint32_t ent = (uint32_t)i | (f32_to_bf16_rne(a[c][e]) << 16);
+          const uint32_t x = topk_key(a[c][e]);
+          if (MA_VALID(i) && (x > T || (x == T && i <= idx_last))) {
+            const uint32_t ent = (uint32_t)i | (window_bf16(f2u(a[c][e]), x) << 16);
             dst[p] = ent;
             if (lds_row) lds_row[p] = ent;
             ++p;
           }
         }
       }
+      // as in the candidate path, a non-finite threshold key is handed on to
+      // the zeroing as +Inf's, exact
+      if (T >= kKeyInf) {
+        T = kKeyInf;
+        exact = true;
+      }
     }
   }
 
   if (!EF) return true;   // no error feedback: codes and statistics are left as they are
 
-  // ---------------- zero the selected entries; block min / max of the residual
+  // ---------------- zero the selected entries; block min / max of the residual.
+  // A non-finite value left after the selection (more than k_b of them in the
+  // block) is dropped from the error feedback: it becomes +0 like a selected
+  // one.  With a finite threshold every non-finite value is selected, and the
+  // float tests below (NaN fails every ordered compare) decide alone; with a
+  // non-finite threshold key only non-finite values are selected and all of
+  // them become 0 either way, which is the exact test against +Inf (the
+  // selection hands such a cut on as T = +Inf's key, exact).
   float mn = __int_as_float(0x7f800000), mx = -__int_as_float(0x7f800000);
   if (exact) {
-    // every element with key T is selected: selected <=> |a| >= T
+    // selected (or dropped) <=> key >= T <=> !(|a| < T)
     const float T_f = u2f(T);
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
@@ -701,7 +761,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       for (int e = 0; e < kChunk; ++e) {
         const int i = c * kChunkSpan + tid * kChunk + e;
         const float x = fabsf(a[c][e]);
-        const bool sel = x > u2f(T) || (x == u2f(T) && i <= idx_last);
+        const bool sel = !(x <= u2f(T)) || (x == u2f(T) && i <= idx_last);
         a[c][e] = sel ? 0.0f : a[c][e];
         if (MA_VALID(i)) {
           mn = fminf(mn, a[c][e]);
@@ -722,6 +782,13 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   }
   mn = mn + 0.0f;   // a zero extreme is stored as +0
   mx = mx + 0.0f;
+  // a range with no finite fp32 value (both signs near the fp32 limit) resets
+  // the block's error feedback: delta = Delta = 0, every code 0 (for the
+  // global pair this is decided on the pair, in global_minmax_kernel)
+  if (QMODE == kQBlock && !(mx - mn <= 3.402823466e38f)) {
+    mn = 0.0f;
+    mx = 0.0f;
+  }
   if (QMODE == kQGlobal1) {
     if (tid == 0) {
       A.blkmm[2 * j] = mn;
@@ -872,6 +939,10 @@ __global__ __launch_bounds__(kThreads) void global_minmax_kernel(const float *bl
     }
     mn = fminf(mn, red[0]);
     mx = fmaxf(mx, red[kWaves]);
+    if (!(mx - mn <= 3.402823466e38f)) {   // no finite range: the error feedback is reset
+      mn = 0.0f;
+      mx = 0.0f;
+    }
     gmm[0] = mn + 0.0f;
     gmm[1] = mx + 0.0f;
   }
@@ -913,9 +984,9 @@ __device__ __forceinline__ void st_param(const ApplyArgs &A, int64_t i, float v)
   else
     __builtin_nontemporal_store(v, A.theta + i);
 }
-constexpr int kThetaPerThread = 8;
+constexpr int kThetaPerThread = 8;   // parameters a thread holds in flight in the sparse update
 constexpr int kMaxWindow = 1024;     // window rows the update kernels take (their factors sit in LDS)
-constexpr int kFusedBeta = 64;       // decay factors of the fused kernel (m <= kFusedEnt / 64 rows)   // parameters a thread holds in flight in the sparse update
+constexpr int kFusedBeta = 64;       // decay factors the fused kernel holds (2m, so m <= 32)
 constexpr int kTouchedSlots = 1024;  // counters the touched-parameter sum is spread over
 
 // LDS of the update: bitmap of touched positions (W words), per-word slot

@@ -4,7 +4,11 @@ oracle on the same seeded inputs and compare them element by element.
 Bars (from the step's definition): Top-k indices, packed 4-bit codes, block
 statistics and the window contents bit-exact; m_hat, v_hat and the updated
 parameters within 1e-6 relative (|gpu - cpu| <= 1e-6 * max(|cpu|, 1e-30)),
-with the bitwise-equal count reported as well."""
+and so is the applied step theta_t - theta_{t-1} relative to the oracle's
+step.  Every path of the library computes these bitwise equal to the oracle
+(same fp32 operations in the same order), and the runners below assert that
+too.  A NaN is compared by class: both sides NaN passes, whatever the payload
+(the hardware's NaN propagation is not part of the method)."""
 from __future__ import annotations
 
 import sys
@@ -46,11 +50,20 @@ def assert_bits_equal(name, got, ref):
 
 
 def assert_close_f32(name, got, ref):
+    """Within 1e-6 relative; returns the number of elements that are not
+    bitwise equal (two NaNs count as equal)."""
     got = np.asarray(got, np.float32).ravel()
     ref = np.asarray(ref, np.float32).ravel()
     assert got.shape == ref.shape, f"{name}: shape {got.shape} != {ref.shape}"
     # bitwise-equal elements pass; the tolerance is checked on the others only
     diff = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    if diff.size == 0:
+        return 0
+    gn, rn = np.isnan(got[diff]), np.isnan(ref[diff])
+    if (gn != rn).any():
+        i = int(diff[np.flatnonzero(gn != rn)[0]])
+        raise AssertionError(f"{name}: NaN on one side only at {i}: gpu={got[i]!r} cpu={ref[i]!r}")
+    diff = diff[~gn]
     if diff.size == 0:
         return 0
     g64 = got[diff].astype(np.float64)
@@ -61,6 +74,27 @@ def assert_close_f32(name, got, ref):
         raise AssertionError(f"{name}: {int((~ok).sum())} outside 1e-6 rel, first at {i}: "
                              f"gpu={got[i]!r} cpu={ref[i]!r}")
     return int(diff.size)
+
+
+def assert_step_close(name, got, ref, prev_got, prev_ref):
+    """The applied step theta_t - theta_{t-1} of each side (in double, from the
+    fp32 values) within 1e-6 of the oracle's step, relative to that step."""
+    got = np.asarray(got, np.float32).ravel().astype(np.float64)
+    ref = np.asarray(ref, np.float32).ravel().astype(np.float64)
+    dg = got - np.asarray(prev_got, np.float32).ravel()
+    dr = ref - np.asarray(prev_ref, np.float32).ravel()
+    fin = np.isfinite(dg) & np.isfinite(dr)
+    bad = fin & ~(np.abs(dg - dr) <= REL_TOL * np.maximum(np.abs(dr), 1e-30))
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{name}: {int(bad.sum())} applied steps outside 1e-6 rel, first at {i}: "
+                             f"gpu step={dg[i]!r} cpu step={dr[i]!r}")
+
+
+def check_theta(name, got, ref, prev_got, prev_ref):
+    n = assert_close_f32(name, got, ref)
+    assert_step_close(name + " step", got, ref, prev_got, prev_ref)
+    return n
 
 
 def to_gpu_bf16(g_bits: np.ndarray, misalign: bool = False):
@@ -98,6 +132,8 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
         g_gpu = to_gpu_bf16(g, misalign)
         say(f"[{label}] step {t}: d={d} B={B} k={k} m={m} wd={wd} flags={flags | gpu_only_flags} "
             f"misalign={misalign} chunks={chunks}")
+        prev_gpu = theta_gpu.cpu().numpy()
+        prev_cpu = theta_cpu.copy()
         opt.step(theta_gpu, g_gpu)
         torch.cuda.synchronize()
         mh, vh = orc.step(theta_cpu, g, moments=True)
@@ -110,7 +146,7 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
             assert_bits_equal(f"{label} t={t} stats", gs, np.broadcast_to(orc.stats.view(np.uint32), gs.shape))
         else:
             assert_bits_equal(f"{label} t={t} stats", opt.stats().view(np.uint32), orc.stats.view(np.uint32))
-        nonbitwise += assert_close_f32(f"{label} t={t} theta", theta_gpu.cpu().numpy(), theta_cpu)
+        nonbitwise += check_theta(f"{label} t={t} theta", theta_gpu.cpu().numpy(), theta_cpu, prev_gpu, prev_cpu)
         if moments:
             gm, gv = opt.moments(mblocks)
             gm, gv = gm.cpu().numpy(), gv.cpu().numpy()
@@ -118,13 +154,17 @@ def full_parity(label, d, B, k, m, steps, *, lr=1e-4, wd=0.0, beta1=0.9, beta2=0
                 s, n = O.block_range(cfg, int(j))
                 nonbitwise += assert_close_f32(f"{label} t={t} m_hat[{j}]", gm[q, :n], mh[s:s + n])
                 nonbitwise += assert_close_f32(f"{label} t={t} v_hat[{j}]", gv[q, :n], vh[s:s + n])
+    assert nonbitwise == 0, f"{label}: {nonbitwise} values within tolerance but not bitwise equal"
     return opt, theta_gpu, theta_cpu, nonbitwise
 
 
-def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_moments=True):
+def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_moments=True, jump=None):
     """Full-size run on the GPU; the oracle follows a deterministic block
     sample (every `every`-th block plus the first and last) exactly, since the
-    blocks are independent."""
+    blocks are independent.  `steps` steps from t = 1; then, if jump =
+    (t0, n), both sides are set to step t0 (ma_set_step, the oracle's t) and
+    run n more, so that late window rows and the wrap of the row index t mod
+    m are written and compared without running t0 steps."""
     w = workload
     d, B, k = w.d, w.block, w.k
     theta = torch.empty(d, dtype=torch.float32, device="cuda")
@@ -144,12 +184,25 @@ def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_m
         states[int(j)] = O.BlockState.zeros(cfg, int(j))
         thetas[int(j)] = th_all[pos:pos + n].copy()
         pos += n
+    schedule = list(range(1, steps + 1))
+    if jump is not None:
+        t0, n_more = jump
+        assert t0 >= steps
+        schedule += list(range(t0 + 1, t0 + n_more + 1))
     nonbitwise = 0
-    for t in range(1, steps + 1):
-        say(f"[{label}] step {t}: {w.name} d={d} m={m} sampled blocks={len(blocks)}")
+    rows_written = set()
+    for t in schedule:
+        if t != opt.t + 1:
+            say(f"[{label}] both sides jump to step {t - 1}")
+            opt.set_step(t - 1)
+            for bs in states.values():
+                bs.t = t - 1
+        rows_written.add(t % m)
+        say(f"[{label}] step {t}: {w.name} d={d} m={m} row {t % m} sampled blocks={len(blocks)}")
         src.fill(g, t)
         torch.cuda.synchronize()
         g_all = g.index_select(0, idx).cpu().numpy().view(np.uint16)
+        th_prev = theta.index_select(0, idx).cpu().numpy()
         opt.step(theta, g)
         torch.cuda.synchronize()
         th_gpu = theta.index_select(0, idx).cpu().numpy()
@@ -162,8 +215,10 @@ def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_m
         for q, (j, (s, n)) in enumerate(zip(blocks, ranges)):
             j = int(j)
             bs = states[j]
+            th_prev_cpu = thetas[j].copy()
             mh, vh = bs.step(thetas[j], g_all[pos:pos + n], moments=True)
-            nonbitwise += assert_close_f32(f"{label} t={t} theta[{j}]", th_gpu[pos:pos + n], thetas[j])
+            nonbitwise += check_theta(f"{label} t={t} theta[{j}]", th_gpu[pos:pos + n], thetas[j],
+                                      th_prev[pos:pos + n], th_prev_cpu)
             pos += n
             off, kb = O.block_quota(cfg, j)
             for i in range(m):
@@ -180,14 +235,16 @@ def sampled_parity(label, workload: synth.Workload, m, steps, every=397, check_m
                 nonbitwise += assert_close_f32(f"{label} t={t} m_hat[{j}]", mh_gpu[q, :n], mh)
                 nonbitwise += assert_close_f32(f"{label} t={t} v_hat[{j}]", vh_gpu[q, :n], vh)
     del opt
-    return nonbitwise
+    assert nonbitwise == 0, f"{label}: {nonbitwise} values within tolerance but not bitwise equal"
+    return rows_written
 
 
-def full_state_parity(label, workload: synth.Workload, m, steps, threads=None):
+def full_state_parity(label, workload: synth.Workload, m, steps, threads=None, jump=None):
     """Full-size run on the GPU against the oracle's whole state: every block,
     the oracle's blocks stepped on several threads (oracle_threads).  After
     every step the window, the codes and the block statistics are compared
-    bit for bit and every parameter within 1e-6 relative."""
+    bit for bit and every parameter (and its applied step) within 1e-6
+    relative, bitwise in fact.  jump = (t0, n): as in sampled_parity."""
     w = workload
     d, B, k = w.d, w.block, w.k
     theta = torch.empty(d, dtype=torch.float32, device="cuda")
@@ -199,20 +256,31 @@ def full_state_parity(label, workload: synth.Workload, m, steps, threads=None):
     torch.cuda.synchronize()
     theta_cpu = theta.cpu().numpy().copy()
     orc = O.FullState(cfg)
+    schedule = list(range(1, steps + 1))
+    if jump is not None:
+        t0, n_more = jump
+        assert t0 >= steps
+        schedule += list(range(t0 + 1, t0 + n_more + 1))
     nonbitwise = 0
-    for t in range(1, steps + 1):
-        say(f"[{label}] step {t}: {w.name} d={d} m={m}, all {opt.num_blocks} blocks")
+    for t in schedule:
+        if t != opt.t + 1:
+            say(f"[{label}] both sides jump to step {t - 1}")
+            opt.set_step(t - 1)
+        say(f"[{label}] step {t}: {w.name} d={d} m={m} row {t % m}, all {opt.num_blocks} blocks")
         src.fill(g, t)
         torch.cuda.synchronize()
         g_cpu = g.cpu().numpy().view(np.uint16)
+        prev_gpu = theta.cpu().numpy()
+        prev_cpu = theta_cpu.copy()
         opt.step(theta, g)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
+        t0_ = time.perf_counter()
         oracle_step_threaded(cfg, t, theta_cpu, g_cpu, orc.ef, orc.stats, orc.G, threads)
-        say(f"[{label}] step {t}: oracle {time.perf_counter() - t0:.1f} s")
+        say(f"[{label}] step {t}: oracle {time.perf_counter() - t0_:.1f} s")
         assert_bits_equal(f"{label} t={t} window", opt.window(), orc.G)
         assert_bits_equal(f"{label} t={t} codes", opt.codes_bytes(), orc.ef)
         assert_bits_equal(f"{label} t={t} stats", opt.stats().view(np.uint32), orc.stats.view(np.uint32))
-        nonbitwise += assert_close_f32(f"{label} t={t} theta", theta.cpu().numpy(), theta_cpu)
+        nonbitwise += check_theta(f"{label} t={t} theta", theta.cpu().numpy(), theta_cpu, prev_gpu, prev_cpu)
     del opt
+    assert nonbitwise == 0, f"{label}: {nonbitwise} values within tolerance but not bitwise equal"
     return nonbitwise

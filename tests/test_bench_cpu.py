@@ -44,9 +44,15 @@ def test_counters_apply_only_to_the_default_step_and_its_kernels():
     assert b.load_traffic("bert_base", 10, False, ["step_fused"]) is None
 
 
-def test_counters_are_dropped_when_the_kernel_source_changes(tmp_path, monkeypatch):
+@pytest.mark.parametrize("which", [0, 1])
+def test_counters_are_dropped_when_the_kernel_source_changes(tmp_path, monkeypatch, which):
+    # a change to the kernels or to the host code that launches them
     b = _bench()
-    src = tmp_path / "kernels.hpp"
-    src.write_text(open(b.KERNEL_SRC).read() + "\n// changed\n")
-    monkeypatch.setattr(b, "KERNEL_SRC", str(src))
+    srcs = list(b.KERNEL_SRCS)
+    changed = tmp_path / os.path.basename(srcs[which])
+    changed.write_text(open(srcs[which]).read() + "\n// changed\n")
+    before = b.kernel_source_sha()
+    srcs[which] = str(changed)
+    monkeypatch.setattr(b, "KERNEL_SRCS", srcs)
+    assert b.kernel_source_sha() != before
     assert b.load_traffic("llama2_7b", 10, False, ["step_fused"]) is None
