@@ -114,6 +114,23 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
 int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate: code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc.  The same step as ma_step (same
+ * arguments, results and errors), with nothing allocated or created per call:
+ * every launch goes to `stream` (no side stream, no timing events), and the
+ * step's scratch (the deferred-block list and its counters, the global
+ * quantizer's per-block min / max and cut) lives in one static device array of
+ * 24 MiB that each device the library runs on holds until the process ends,
+ * instead of the handle's buffers.  Handles of more than 2^20 blocks are
+ * rejected with MA_EUNSUPPORTED before anything is launched; MA_EHIP if the
+ * array's device address could not be looked up when the handle was created.
+ * Every call on one device shares that array and leaves its contents behind
+ * (the step clears what must start at zero), so ma_step_noalloc calls that
+ * overlap on one device race, even on different handles and streams.
+ */
+int ma_step_noalloc(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream);
+
+/*
  * Comparison baseline: one fp32 AdamW step (the 8d-byte optimizer the second
  * paragraph compares against), stateless, on caller-owned device arrays of n
  * elements: theta, m, v fp32 (updated in place), grads bf16 (raw bits).  Step t

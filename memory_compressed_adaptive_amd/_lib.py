@@ -30,7 +30,7 @@ MA_STATE_WINDOW = 2
 
 # every symbol include/microadam.h declares
 EXPORTS = (
-    "ma_create", "ma_step", "ma_step_bf16", "ma_adamw_step", "ma_adamw8_step", "ma_state_bytes", "ma_aux_bytes", "ma_destroy", "ma_last_error",
+    "ma_create", "ma_step", "ma_step_bf16", "ma_step_noalloc", "ma_adamw_step", "ma_adamw8_step", "ma_state_bytes", "ma_aux_bytes", "ma_destroy", "ma_last_error",
     "ma_last_error_message", "ma_get_step", "ma_num_blocks", "ma_set_step", "ma_set_flags",
     "ma_set_lr", "ma_read_state", "ma_write_state", "ma_debug_moments", "ma_debug_residual", "ma_set_timing",
     "ma_kernel_times", "ma_set_pipeline", "ma_get_pipeline", "ma_set_count_touched", "ma_touched_count",
@@ -64,6 +64,8 @@ def lib():
     L.ma_adamw8_step.argtypes = [i64, i64, f32, f32, f32, f32, f32, p, p, p, p, p, p, p]
     L.ma_step_bf16.restype = C.c_int
     L.ma_step_bf16.argtypes = [p, p, p, p]
+    L.ma_step_noalloc.restype = C.c_int
+    L.ma_step_noalloc.argtypes = [p, p, p, p]
     L.ma_state_bytes.restype = C.c_size_t
     L.ma_state_bytes.argtypes = [p]
     L.ma_aux_bytes.restype = C.c_size_t

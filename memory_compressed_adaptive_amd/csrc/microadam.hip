@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -41,6 +42,44 @@ void clear_error() {
 // beats one pass at two workgroups per CU (and smaller budgets, with more
 // passes, are slower again).
 constexpr size_t kApplyLdsLimit = 53 * 1024 - 512;
+
+// ---------------------------------------------------------------- ma_step_noalloc's scratch
+// The per-step scratch of ma_step_noalloc lives in one file-scope device
+// array, which each device the library runs on holds until the process ends:
+// the compressor's deferred-block list (int64 per block) and its counters, and
+// the global quantizer's per-block min / max (2 f32 per block), cut (2 u32 per
+// block) and global pair.  Sized for kNoAllocMaxBlocks blocks: 24 MiB.  In
+// host code `scratch` names a host-side stand-in; kernels get the device
+// address from hipGetSymbolAddress, taken once per device.
+constexpr int64_t kNoAllocMaxBlocks = int64_t(1) << 20;
+constexpr size_t kNaDeferred = 0;                                  // int64[kNoAllocMaxBlocks]
+constexpr size_t kNaCounts = kNaDeferred + 8 * kNoAllocMaxBlocks;  // u32[64]
+constexpr size_t kNaBlkmm = kNaCounts + 256;                       // f32[2 * kNoAllocMaxBlocks]
+constexpr size_t kNaSelinfo = kNaBlkmm + 8 * kNoAllocMaxBlocks;    // u32[2 * kNoAllocMaxBlocks]
+constexpr size_t kNaGmm = kNaSelinfo + 8 * kNoAllocMaxBlocks;      // f32[2]
+constexpr size_t kNoAllocScratchBytes = kNaGmm + 256;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev` (which must be current),
+// looked up once per device; nullptr if the lookup fails.
+void *noalloc_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -78,6 +117,10 @@ struct ma_ctx {
 
   // last step's constants (for ma_debug_moments)
   float last_c1 = 0, last_c2 = 0;
+
+  // device address of ma_step_noalloc's scratch on this handle's device
+  // (looked up at create; nullptr if that failed)
+  unsigned char *na_scratch = nullptr;
 
   // overlap of compress and update across block ranges (see ma_step)
   int chunks = 1;
@@ -529,6 +572,9 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     fail(MA_EHIP, "initialising the optimizer state failed: %s", hipGetErrorString(e));
     return nullptr;
   }
+  // ma_step_noalloc's scratch: its address on this device, once per device
+  // (a failure here only disables ma_step_noalloc on this handle)
+  h->na_scratch = static_cast<unsigned char *>(noalloc_scratch(h->device));
   return h;
 }
 
@@ -579,15 +625,31 @@ int ma_set_lr(ma_ctx *h, float lr) {
 
 namespace {
 
-// One step for fp32 (bf false) or bfloat16 (bf true) parameters.
-int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream_t stream) {
+// One step for fp32 (bf false) or bfloat16 (bf true) parameters.  noalloc:
+// the ma_step_noalloc variant: the step's scratch comes from the static
+// `scratch` array instead of the handle's buffers, and every launch goes to
+// `stream` (no side stream, no events): nothing is created or allocated.
+int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream_t stream, bool noalloc = false) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_step: null handle");
   if (!params || !grads) return fail(MA_EINVAL, "ma_step: null params or grads");
   if (((uintptr_t)params & (bf ? 1u : 3u)) || ((uintptr_t)grads & 1u))
     return fail(MA_EINVAL, "ma_step: params must be element-aligned and grads 2-byte aligned");
+  if (noalloc && h->n_b > kNoAllocMaxBlocks)
+    return fail(MA_EUNSUPPORTED, "ma_step_noalloc: %lld blocks exceed its static scratch of %lld blocks",
+                (long long)h->n_b, (long long)kNoAllocMaxBlocks);
+  if (noalloc && !h->na_scratch)
+    return fail(MA_EHIP, "ma_step_noalloc: the address of its scratch on device %d is unknown", h->device);
   DeviceGuard guard(h->device);
   if (!guard.ok) return fail(MA_EHIP, "ma_step: cannot select device %d", h->device);
+  // the step's scratch: the deferred-block list and counters, the global
+  // quantizer's per-block min / max, cut and pair
+  int64_t *q_deferred = noalloc ? reinterpret_cast<int64_t *>(h->na_scratch + kNaDeferred) : h->deferred;
+  unsigned int *q_counts = noalloc ? reinterpret_cast<unsigned int *>(h->na_scratch + kNaCounts) : h->n_deferred;
+  float *q_blkmm = noalloc ? reinterpret_cast<float *>(h->na_scratch + kNaBlkmm) : h->blkmm;
+  uint32_t *q_selinfo = noalloc ? reinterpret_cast<uint32_t *>(h->na_scratch + kNaSelinfo) : h->selinfo;
+  float *q_gmm = noalloc ? reinterpret_cast<float *>(h->na_scratch + kNaGmm) : h->gmm;
+  const bool timing = h->timing && !noalloc;
 
   const int64_t t = h->t + 1;
   const double b1 = (double)h->beta1, b2 = (double)h->beta2;
@@ -608,8 +670,8 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   ca.row_base = (t % h->m) * h->k;
   ca.seed = h->seed;
   ca.B = h->B;
-  ca.deferred = h->deferred;
-  ca.n_deferred = h->n_deferred;
+  ca.deferred = q_deferred;
+  ca.n_deferred = q_counts;
 
   ApplyArgs aa = make_apply_args(h, t, c1, c2, decay);
   aa.theta = bf ? nullptr : static_cast<float *>(params);
@@ -643,16 +705,14 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   // concurrently on the side stream, the update, which reads only the window
   // and the parameters: neither writes what the other reads.
   if (ef && (h->flags & MA_FLAG_GLOBAL_QUANT)) {
-    ca.blkmm = h->blkmm;
-    ca.selinfo = h->selinfo;
-    ca.gmm = h->gmm;
-    if (!ensure_pipeline(h, 1)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
+    ca.blkmm = q_blkmm;
+    ca.selinfo = q_selinfo;
+    ca.gmm = q_gmm;
+    if (!noalloc && !ensure_pipeline(h, 1)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
     hipEvent_t tg[6] = {};
-    if (h->timing && !take_events(h, tg, 6)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (timing && !take_events(h, tg, 6)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     hipEvent_t t0 = tg[0], t1 = tg[1], t2 = tg[2], t3 = tg[3], t4 = tg[4], t5 = tg[5];
-    ca.deferred = h->deferred;
-    ca.n_deferred = h->n_deferred;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, 1);
     // Full blocks: the first pass fused with the update (the update needs only
     // the block's window, which the first pass completes), then the second
     // pass alone.  Neither writes what the other reads.  The dense update
@@ -672,6 +732,17 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
         h->pool.push_back(t4);
         h->pool.push_back(t5);
       }
+      if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
+      h->t = t;
+      h->last_c1 = c1;
+      h->last_c2 = c2;
+      return MA_OK;
+    }
+    if (noalloc) {
+      // everything on the caller's stream: pass 1, the update, pass 2
+      e = dispatch_global_p1(h->cpt, g_al, ca, h->n_b, n_full, stream);
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream, bf);
+      if (e == hipSuccess) e = dispatch_global_p2(h->cpt, g_al, ca, 0, h->n_b, n_full, stream);
       if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
       h->t = t;
       h->last_c1 = c1;
@@ -714,12 +785,10 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   // a partial last block (if any) runs the two kernels after it.  The dense
   // update (decoupled decay) is fused for 16-byte aligned parameters.
   if (h->fused_ok && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
-    ca.deferred = h->deferred;
-    ca.n_deferred = h->n_deferred;
     hipEvent_t tf[2] = {};
-    if (h->timing && !take_events(h, tf, 2)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
+    if (timing && !take_events(h, tf, 2)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     hipEvent_t t0 = tf[0], t1 = tf[1];
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, 1);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, 1);
     e = hipGetLastError();
     if (t0) (void)hipEventRecord(t0, stream);
     if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, mode == kModeDense, ca, aa, n_full, h->apply_lds, stream, bf);
@@ -740,10 +809,10 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     return MA_OK;
   }
 
-  const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
+  const int chunks = noalloc ? 1 : (int)std::max<int64_t>(1, std::min<int64_t>(h->chunks, h->n_b));
   if (chunks > 1 && !ensure_pipeline(h, chunks)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
   // per range: compress start / end, update start / end
-  std::vector<hipEvent_t> tp(h->timing ? 4 * (size_t)chunks : 0, nullptr);
+  std::vector<hipEvent_t> tp(timing ? 4 * (size_t)chunks : 0, nullptr);
   if (!tp.empty() && !take_events(h, tp.data(), (int)tp.size())) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
   hipStream_t upd = chunks > 1 ? h->side : stream;
   if (chunks > 1) {
@@ -752,14 +821,14 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   }
   // every range's deferred-block counter starts at zero
   if (e == hipSuccess && n_full > 0) {
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, h->n_deferred, chunks);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, chunks);
     e = hipGetLastError();
   }
   for (int i = 0; i < chunks && e == hipSuccess; ++i) {
     const int64_t b0 = h->n_b * i / chunks, b1 = h->n_b * (i + 1) / chunks;
     CompressArgs cai = ca;
-    cai.deferred = h->deferred + b0;
-    cai.n_deferred = h->n_deferred + i;
+    cai.deferred = q_deferred + b0;
+    cai.n_deferred = q_counts + i;
     hipEvent_t t0 = tp.empty() ? nullptr : tp[4 * (size_t)i], t1 = tp.empty() ? nullptr : tp[4 * (size_t)i + 1];
     if (t0) (void)hipEventRecord(t0, stream);
     e = dispatch_compress(h->cpt, g_al, ef, cai, b0, b1, n_full, stream);
@@ -808,6 +877,10 @@ int ma_step(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream)
 
 int ma_step_bf16(ma_ctx *h, uint16_t *params, const uint16_t *grads, hipStream_t stream) {
   return step_impl(h, params, true, grads, stream);
+}
+
+int ma_step_noalloc(ma_ctx *h, float *params, const uint16_t *grads, hipStream_t stream) {
+  return step_impl(h, params, false, grads, stream, true);
 }
 
 int ma_adamw_step(int64_t n, int64_t t, float beta1, float beta2, float eps, float lr, float wd, float *theta,
