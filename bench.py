@@ -64,6 +64,170 @@ def load_traffic(workload: str, m: int, variant: bool, kernels):
     return t
 
 
+def oracle_follow(cfg, blocks, ranges, th0, grads, bf16=False):
+    """The CPU oracle (single-threaded) on the sampled blocks through every
+    step: th0 the blocks' initial parameters (concatenated), grads the list of
+    each step's gradients of those blocks.  Returns the blocks' states, their
+    parameters and the seconds it took."""
+    import numpy as np
+    import oracle as O
+    states = {int(j): O.BlockState.zeros(cfg, int(j)) for j in blocks}
+    ths, pos = [], 0
+    for (s0, n) in ranges:
+        ths.append(th0[pos:pos + n].copy())
+        pos += n
+    c0 = time.perf_counter()
+    for gh in grads:
+        pos = 0
+        for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
+            if bf16:
+                # widen, fp32 step, round to nearest even once
+                th32 = O.bf16_to_f32(ths[q]).astype(np.float32)
+                states[int(j)].step(th32, gh[pos:pos + n])
+                ths[q] = O.bf16_rne(th32)
+            else:
+                states[int(j)].step(ths[q], gh[pos:pos + n])
+            pos += n
+    return states, ths, time.perf_counter() - c0
+
+
+def sampled_parity_check(opt, cfg, blocks, ranges, th_gpu, states, ths, bf16=False):
+    """The sampled blocks' parameters, codes, statistics and window rows of the
+    GPU run against the oracle's after the same steps."""
+    import numpy as np
+    import oracle as O
+    m, k = cfg.m, cfg.k
+    stats_gpu = opt.stats()
+    bad = {"theta": 0, "codes": 0, "stats": 0, "window": 0}
+    nonbitwise = 0
+    pos = 0
+    for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
+        j = int(j)
+        bs = states[j]
+        got = th_gpu[pos:pos + n]
+        ref = ths[q]
+        pos += n
+        if bf16:
+            same = got == ref
+            close = same
+        else:
+            same = (got.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(got) & np.isnan(ref))
+            close = np.abs(got.astype(np.float64) - ref) <= 1e-6 * np.maximum(np.abs(ref), 1e-30)
+        bad["theta"] += int((~(same | close)).sum())
+        nonbitwise += int((~same).sum())
+        codes = O.unpack_nibbles(opt.codes_bytes(s0 >> 1, ((s0 & 1) + n + 1) // 2), n, s0 & 1)
+        bad["codes"] += int((codes != bs.codes()).sum())
+        bad["stats"] += int((stats_gpu[2 * j:2 * j + 2].view(np.uint32) != bs.stats.view(np.uint32)).sum())
+        off, kb = O.block_quota(cfg, j)
+        for i in range(m):
+            bad["window"] += int((opt.window(i * k + off, kb) != bs.gseg[i]).sum())
+    return {"blocks": len(blocks), "ok": not any(bad.values()) and nonbitwise == 0, "mismatches": bad,
+            "theta_not_bitwise": nonbitwise}
+
+
+def traffic_for(workload, m, kern_names):
+    """Counter bytes per step from a committed summary that matches the current
+    source and the kernels this run used, else None."""
+    t = load_traffic(workload, m, False, kern_names)
+    if t is None:
+        return None
+    return sum(v["fetch_bytes"] + v["write_bytes"] for v in t["kernels"].values())
+
+
+# The five workloads of the step's configurations, at 1 GPU: each at its own
+# window and step count (LLaMA-2-13B over the window sweep).  The headline
+# line is LLaMA-2-7B; these are reported beside it in "configs".
+CONFIG_RUNS = [("tiny", 10), ("bert_base", 10), ("opt_1_3b", 10), ("llama2_13b", 1), ("llama2_13b", 10),
+               ("llama2_13b", 20), ("llama2_13b", 37)]
+
+
+def run_config(name, m, dev, copy_gbps, oracle_block_steps=1200, cpu_leg=True):
+    """One configuration: m steps fill the window, 2 warmup steps, then the
+    configuration's step count K.  Every step takes fresh gradients from the
+    generator, produced before the step and outside its timing: each timed
+    step is bracketed by HIP events on the step's stream.  The oracle follows a
+    block sample through every step (parity and its extrapolated rate)."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from memory_compressed_adaptive_amd import MicroAdam
+    from memory_compressed_adaptive_amd import synth
+
+    w = synth.WORKLOADS[name]
+    d, B, k = w.d, w.block, w.k
+    K, W = w.steps, 2
+    n_all = m + W + K
+    theta = torch.empty(d, dtype=torch.float32, device=dev)
+    synth.fill_params(theta)
+    g = torch.empty(d, dtype=torch.int16, device=dev)
+    gsrc = synth.GradSource(w)
+    opt = MicroAdam(d, B, k, m)
+    nb = opt.num_blocks
+    cfg = O.make_cfg(d, B, k, m)
+    every = max(1, nb // max(8, oracle_block_steps // n_all))
+    blocks = synth.sample_blocks(nb, every)
+    ranges = [(int(j) * B, min(B, d - int(j) * B)) for j in blocks]
+    idx = torch.from_numpy(np.concatenate([np.arange(s, s + n) for s, n in ranges])).to(dev)
+    th0 = theta.index_select(0, idx).cpu().numpy()
+    grads = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for s in range(n_all):
+        gsrc.fill(g, s + 1)
+        if cpu_leg:
+            grads.append(g.index_select(0, idx).cpu().numpy().view(np.uint16))
+        i = s - (m + W)
+        if i == 0:
+            torch.cuda.synchronize()
+            opt.set_timing(True)
+            opt.set_count_touched(True)
+        if i >= 0:
+            evs[i][0].record()
+        opt.step(theta, g)
+        if i >= 0:
+            evs[i][1].record()
+    torch.cuda.synchronize()
+    ms_steps = [a.elapsed_time(b) for a, b in evs]
+    ms = sum(ms_steps) / K
+    kt = opt.kernel_times()
+    touched = opt.touched_count() / K
+    opt.set_count_touched(False)
+    opt.set_timing(False)
+    fused = kt["step_fused"][1] > 0
+    kern_names = [n for n in ("step_fused", "compress", "adamstats_apply") if kt[n][1] > 0]
+    bytes_step = 2 * d + 2 * ((d + 1) // 2) + 4 * k + 16 * nb + 4 * m * k + 8 * touched
+    sps = 1e3 / ms
+    out = {"workload": name, "d": d, "m": m, "k": k, "steps": K, "ms_per_step": round(ms, 4),
+           "steps_per_s": round(sps, 2), "params_per_s": round(d * sps, 1),
+           "path": "fused" if fused else "two-kernel",
+           "algorithmic_GB_per_step": round(bytes_step / 1e9, 4),
+           "algorithmic_GBps": round(bytes_step * sps / 1e9, 1),
+           "algorithmic_frac_of_peak": round(bytes_step * sps / 1e9 / HBM_PEAK_GBPS, 4),
+           "touched_fraction": round(touched / d, 5),
+           "kernels_ms_per_step": {n: round(kt[n][0] / K, 4) for n in kt if kt[n][1] > 0}}
+    cb = traffic_for(name, m, kern_names)
+    out["counter_GB_per_step"] = None if cb is None else round(cb / 1e9, 3)
+    out["counter_GBps"] = None if cb is None else round(cb * sps / 1e9, 1)
+    out["counter_frac_of_peak"] = None if cb is None else round(cb * sps / 1e9 / HBM_PEAK_GBPS, 4)
+    out["counter_frac_of_copy"] = None if cb is None else round(cb * sps / 1e9 / copy_gbps, 4)
+    if cpu_leg:
+        th_gpu = theta.index_select(0, idx).cpu().numpy()
+        states, ths, secs = oracle_follow(cfg, blocks, ranges, th0, grads)
+        out["parity_sampled"] = dict(sampled_parity_check(opt, cfg, blocks, ranges, th_gpu, states, ths),
+                                     steps=n_all)
+        out["cpu_baseline"] = {"value": round(1.0 / (secs / (len(blocks) * n_all) * nb), 6), "unit": "steps/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{len(blocks)} of {nb} blocks x {n_all} steps, {secs:.1f} s, "
+                                         f"extrapolated to all blocks"}
+    opt.close()
+    del theta, g, gsrc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"config {name} m={m}: {sps:.2f} steps/s ({ms:.3f} ms), {out['algorithmic_GBps']} GB/s algorithmic, "
+        f"parity ok={out.get('parity_sampled', {}).get('ok')}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +250,8 @@ def main():
                     help="one (delta, Delta) over all d (two compressor passes); no oracle leg")
     ap.add_argument("--chunks", type=int, default=0,
                     help="block ranges whose update overlaps the next range's compression (0: library default)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (the `configs` array of the default line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -295,63 +461,29 @@ def main():
         th_gpu = theta.index_select(0, idx).cpu().numpy()
         if args.bf16_params:
             th_gpu = th_gpu.view(np.uint16)
-        stats_gpu = opt.stats()
         cfg = O.make_cfg(d, B, k, m, wd=args.wd)
-        states = {int(j): O.BlockState.zeros(cfg, int(j)) for j in blocks}
-        ths = []
-        pos = 0
-        for (s, n) in ranges:
-            ths.append(th0[pos:pos + n].copy())
-            pos += n
-        c0 = time.perf_counter()
-        for s in range(n_pre + K):
-            gh = g_host[s % P]
-            pos = 0
-            for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
-                if args.bf16_params:
-                    # widen, fp32 step, round to nearest even once
-                    th32 = O.bf16_to_f32(ths[q]).astype(np.float32)
-                    states[int(j)].step(th32, gh[pos:pos + n])
-                    ths[q] = O.bf16_rne(th32)
-                else:
-                    states[int(j)].step(ths[q], gh[pos:pos + n])
-                pos += n
-        c1 = time.perf_counter()
-        per_block_step = (c1 - c0) / (len(blocks) * (n_pre + K))
+        states, ths, secs = oracle_follow(cfg, blocks, ranges, th0, [g_host[s % P] for s in range(n_pre + K)],
+                                          bf16=args.bf16_params)
+        per_block_step = secs / (len(blocks) * (n_pre + K))
         cpu_steps_per_s = 1.0 / (per_block_step * nb)
         result["cpu_baseline"] = {
             "value": round(cpu_steps_per_s, 6), "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(blocks)} of {nb} blocks (every {every}th, plus first and last) x {n_pre + K} steps "
-                      f"of {w.name}; {c1 - c0:.1f} s single-threaded, extrapolated to all blocks",
+                      f"of {w.name}; {secs:.1f} s single-threaded, extrapolated to all blocks",
             "host_cpus": os.cpu_count()}
-        # parity of the sampled blocks after the whole run
-        bad = {"theta": 0, "codes": 0, "stats": 0, "window": 0}
-        nonbitwise = 0
-        pos = 0
-        for q, (j, (s0, n)) in enumerate(zip(blocks, ranges)):
-            j = int(j)
-            bs = states[j]
-            got = th_gpu[pos:pos + n]
-            ref = ths[q]
-            pos += n
-            if args.bf16_params:
-                same = got == ref
-                close = same
-            else:
-                same = got.view(np.uint32) == ref.view(np.uint32)
-                close = np.abs(got.astype(np.float64) - ref) <= 1e-6 * np.maximum(np.abs(ref), 1e-30)
-            bad["theta"] += int((~(same | close)).sum())
-            nonbitwise += int((~same).sum())
-            codes = O.unpack_nibbles(opt.codes_bytes(s0 >> 1, ((s0 & 1) + n + 1) // 2), n, s0 & 1)
-            bad["codes"] += int((codes != bs.codes()).sum())
-            bad["stats"] += int((stats_gpu[2 * j:2 * j + 2].view(np.uint32) != bs.stats.view(np.uint32)).sum())
-            off, kb = O.block_quota(cfg, j)
-            for i in range(m):
-                bad["window"] += int((opt.window(i * k + off, kb) != bs.gseg[i]).sum())
-        result["parity_sampled"] = {"blocks": len(blocks), "steps": n_pre + K, "ok": not any(bad.values()),
-                                    "mismatches": bad, "theta_not_bitwise": nonbitwise}
+        result["parity_sampled"] = dict(sampled_parity_check(opt, cfg, blocks, ranges, th_gpu, states, ths,
+                                                             bf16=args.bf16_params), steps=n_pre + K)
         log(f"cpu baseline {cpu_steps_per_s:.5f} steps/s (extrapolated); parity ok={result['parity_sampled']['ok']}")
 
+    # ---------------- the other configurations, one after another
+    default_line = not (args.dense or args.global_quant or args.bf16_params or args.wd or args.chunks
+                        or args.m or args.workload != "llama2_7b")
+    if default_line and not args.no_configs:
+        opt.close()
+        del theta, pool
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["configs"] = [run_config(nm, mm, dev, copy_gbps, cpu_leg=cpu_leg) for nm, mm in CONFIG_RUNS]
     opt.close()
     print(json.dumps(result), flush=True)
 
