@@ -42,6 +42,8 @@ void clear_error() {
 // beats one pass at two workgroups per CU (and smaller budgets, with more
 // passes, are slower again).
 constexpr size_t kApplyLdsLimit = 53 * 1024 - 512;
+// step_csu_kernel's LDS buffer (three workgroups per CU)
+constexpr size_t kFusedCsuLdsLimit = 4 * (size_t)kFusedCsuWords;
 
 // ---------------------------------------------------------------- ma_step_noalloc's scratch
 // The per-step scratch of ma_step_noalloc lives in one file-scope device
@@ -99,6 +101,12 @@ struct ma_ctx {
   bool dense_default = false;   // stream the parameters in the update even without decay
   size_t apply_lds = 0;
   bool fused_ok = false;   // the block's window fits the fused kernel's LDS (kFusedEnt)
+  bool csu_ok = false;     // the column-sorted update takes this shape (entries per thread, LDS)
+  size_t csu_lds = 0;      // its dynamic LDS
+  int32_t csu_slots = 0;
+  bool fused_csu_ok = false;   // full blocks fit step_csu_kernel (three workgroups per CU)
+  size_t fused_csu_lds = 0;
+  int32_t fused_union_words = 0;
 
   uint8_t *codes = nullptr;
   size_t codes_bytes = 0, codes_alloc = 0;
@@ -263,22 +271,37 @@ hipError_t dispatch_compress(int cpt, bool aligned, bool ef, const CompressArgs 
   }
 }
 
+// How the update runs: the column-sorted kernels (csu) or the row-by-row
+// ones, with the dynamic LDS of the kind chosen.
+struct UpdLaunch {
+  bool csu;
+  size_t lds;
+  bool fused_csu;      // full blocks: step_csu_kernel instead of step_full_kernel
+  size_t fused_lds;    // its dynamic LDS
+};
+
 template <int CPT, int MODE, bool AL, bool BF>
-hipError_t launch_apply(const ApplyArgs &a, int64_t grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((apply_kernel<CPT, MODE, AL, BF>), dim3((unsigned)grid), dim3(kThreads), lds, s, a);
+hipError_t launch_apply(const ApplyArgs &a, int64_t grid, const UpdLaunch &u, hipStream_t s) {
+  if (u.csu)
+    hipLaunchKernelGGL((apply_csu_kernel<CPT, MODE, AL, BF>), dim3((unsigned)grid), dim3(kThreads), u.lds, s, a);
+  else
+    hipLaunchKernelGGL((apply_kernel<CPT, MODE, AL, BF>), dim3((unsigned)grid), dim3(kThreads), u.lds, s, a);
   return hipGetLastError();
 }
 
 template <int CPT, bool BF>
-hipError_t launch_apply_cpt(int mode, bool aligned, const ApplyArgs &a, int64_t grid, size_t lds, hipStream_t s) {
-  if (mode == kModeSparse) return launch_apply<CPT, kModeSparse, false, BF>(a, grid, lds, s);
+hipError_t launch_apply_cpt(int mode, bool aligned, const ApplyArgs &a, int64_t grid, const UpdLaunch &lds,
+                            hipStream_t s) {
+  if (mode == kModeSparse)
+    return aligned ? launch_apply<CPT, kModeSparse, true, BF>(a, grid, lds, s)
+                   : launch_apply<CPT, kModeSparse, false, BF>(a, grid, lds, s);
   if (mode == kModeMoments) return launch_apply<CPT, kModeMoments, false, false>(a, grid, lds, s);
   return aligned ? launch_apply<CPT, kModeDense, true, BF>(a, grid, lds, s)
                  : launch_apply<CPT, kModeDense, false, BF>(a, grid, lds, s);
 }
 
 // bf: the parameters are bfloat16 (ApplyArgs::theta16)
-hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, int64_t grid, size_t lds,
+hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, int64_t grid, const UpdLaunch &lds,
                           hipStream_t s, bool bf = false) {
   switch (cpt) {
     case 1: return bf ? launch_apply_cpt<1, true>(mode, aligned, a, grid, lds, s) : launch_apply_cpt<1, false>(mode, aligned, a, grid, lds, s);
@@ -292,23 +315,31 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
 // deferred (compress, then update, from the device list).  QMODE kQGlobal1:
 // the global quantizer's first pass in place of the compressor.
 template <int CPT, bool EF, bool BF, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
-hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  // the kernel's LDS holds at most kFusedBeta decay factors (2m)
-  if (2 * (int64_t)a.m > kFusedBeta) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0, s,
-                     c, a, (int64_t)0);
+hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
+  if (apply_lds.fused_csu) {
+    hipLaunchKernelGGL((step_csu_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0,
+                       s, c, a, (int64_t)0);
+  } else {
+    // the kernel's LDS holds at most kFusedBeta decay factors (2m)
+    if (2 * (int64_t)a.m > kFusedBeta) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((step_full_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0,
+                       s, c, a, (int64_t)0);
+  }
   const unsigned grid2 = (unsigned)std::min<int64_t>(n_full, 256);
   hipLaunchKernelGGL((compress_deferred_kernel<CPT, EF, QMODE>), dim3(grid2), dim3(kThreads), 0, s, c);
   ApplyArgs al = a;
   al.blocks = c.deferred;
   al.n_list = c.n_deferred;
-  hipLaunchKernelGGL((apply_list_kernel<CPT, BF, MODE>), dim3(grid2), dim3(kThreads), apply_lds, s, al);
+  if (apply_lds.csu)
+    hipLaunchKernelGGL((apply_csu_list_kernel<CPT, BF, MODE>), dim3(grid2), dim3(kThreads), apply_lds.lds, s, al);
+  else
+    hipLaunchKernelGGL((apply_list_kernel<CPT, BF, MODE>), dim3(grid2), dim3(kThreads), apply_lds.lds, s, al);
   return hipGetLastError();
 }
 
 template <bool BF>
-hipError_t dispatch_fused_t(int cpt, bool ef, bool dense, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
-                            size_t apply_lds, hipStream_t s) {
+hipError_t dispatch_fused_t(int cpt, bool ef, bool dense, bool p_al, const CompressArgs &c, const ApplyArgs &a,
+                            int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
   if (dense) {   // decoupled decay: every parameter streamed (aligned parameters only)
     switch (cpt) {
       case 1: return ef ? launch_fused<1, true, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s)
@@ -319,6 +350,19 @@ hipError_t dispatch_fused_t(int cpt, bool ef, bool dense, const CompressArgs &c,
                          : launch_fused<4, false, BF, kQBlock, kModeDense, true>(c, a, n_full, apply_lds, s);
     }
   }
+  // sparse: 16-byte aligned parameters go through the column-sorted update's
+  // vector loads and stores (the row-by-row update gathers single parameters
+  // either way)
+  if (p_al && apply_lds.fused_csu) {
+    switch (cpt) {
+      case 1: return ef ? launch_fused<1, true, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s)
+                        : launch_fused<1, false, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s);
+      case 2: return ef ? launch_fused<2, true, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s)
+                        : launch_fused<2, false, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s);
+      default: return ef ? launch_fused<4, true, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s)
+                         : launch_fused<4, false, BF, kQBlock, kModeSparse, true>(c, a, n_full, apply_lds, s);
+    }
+  }
   switch (cpt) {
     case 1: return ef ? launch_fused<1, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<1, false, BF>(c, a, n_full, apply_lds, s);
     case 2: return ef ? launch_fused<2, true, BF>(c, a, n_full, apply_lds, s) : launch_fused<2, false, BF>(c, a, n_full, apply_lds, s);
@@ -326,10 +370,10 @@ hipError_t dispatch_fused_t(int cpt, bool ef, bool dense, const CompressArgs &c,
   }
 }
 
-hipError_t dispatch_fused(int cpt, bool ef, bool dense, const CompressArgs &c, const ApplyArgs &a, int64_t n_full,
-                          size_t apply_lds, hipStream_t s, bool bf) {
-  return bf ? dispatch_fused_t<true>(cpt, ef, dense, c, a, n_full, apply_lds, s)
-            : dispatch_fused_t<false>(cpt, ef, dense, c, a, n_full, apply_lds, s);
+hipError_t dispatch_fused(int cpt, bool ef, bool dense, bool p_al, const CompressArgs &c, const ApplyArgs &a,
+                          int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s, bool bf) {
+  return bf ? dispatch_fused_t<true>(cpt, ef, dense, p_al, c, a, n_full, apply_lds, s)
+            : dispatch_fused_t<false>(cpt, ef, dense, p_al, c, a, n_full, apply_lds, s);
 }
 
 // The global quantizer's launches over all blocks: pass 1 (full aligned
@@ -378,7 +422,7 @@ hipError_t dispatch_global_p1(int cpt, bool aligned, const CompressArgs &a, int6
 // blocks.  The second pass follows on the same stream.
 template <int CPT, bool BF, int MODE, bool PAL>
 hipError_t launch_fused_global1(const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al, int64_t n_b,
-                                int64_t n_full, size_t apply_lds, hipStream_t s) {
+                                int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
   hipError_t e = launch_fused<CPT, true, BF, kQGlobal1, MODE, PAL>(c, a, n_full, apply_lds, s);
   if (e == hipSuccess && n_b > n_full) {
     hipLaunchKernelGGL((compress_kernel<CPT, true, true, kQGlobal1>), dim3((unsigned)(n_b - n_full)), dim3(kThreads), 0,
@@ -394,7 +438,7 @@ hipError_t launch_fused_global1(const CompressArgs &c, const ApplyArgs &a, int m
 
 template <int MODE, bool PAL>
 hipError_t dispatch_fused_global1_t(int cpt, bool bf, const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al,
-                                    int64_t n_b, int64_t n_full, size_t apply_lds, hipStream_t s) {
+                                    int64_t n_b, int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
   switch (cpt) {
     case 1: return bf ? launch_fused_global1<1, true, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s)
                       : launch_fused_global1<1, false, MODE, PAL>(c, a, mode, p_al, n_b, n_full, apply_lds, s);
@@ -407,9 +451,11 @@ hipError_t dispatch_fused_global1_t(int cpt, bool bf, const CompressArgs &c, con
 
 // mode kModeDense requires 16-byte aligned parameters (p_al)
 hipError_t dispatch_fused_global1(int cpt, bool bf, const CompressArgs &c, const ApplyArgs &a, int mode, bool p_al,
-                                  int64_t n_b, int64_t n_full, size_t apply_lds, hipStream_t s) {
-  return mode == kModeDense
-             ? dispatch_fused_global1_t<kModeDense, true>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s)
+                                  int64_t n_b, int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
+  if (mode == kModeDense)
+    return dispatch_fused_global1_t<kModeDense, true>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s);
+  return (p_al && apply_lds.fused_csu)
+             ? dispatch_fused_global1_t<kModeSparse, true>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s)
              : dispatch_fused_global1_t<kModeSparse, false>(cpt, bf, c, a, mode, p_al, n_b, n_full, apply_lds, s);
 }
 
@@ -439,6 +485,21 @@ hipError_t dispatch_global_p2(int cpt, bool aligned, const CompressArgs &a, int6
 }
 
 
+// The update kernels a handle uses: column-sorted where the block's window
+// fits them, unless MA_FLAG_ROW_SUMS asks for the row-by-row sums.
+// Full blocks run step_full_kernel (row-by-row sums, window preloaded during
+// the compressor's staging) where its LDS holds the window, and
+// step_csu_kernel where only the column-sorted update fits (longer windows).
+// Measured at LLaMA-2 shapes: step_full_kernel is faster at m <= 10 (13B:
+// 16.7 vs 21.5 ms at m = 1, 25.4 vs 29.2 ms at m = 10), step_csu_kernel at
+// m = 20 and 37 (33.3 and 38.8 ms against 33.7 and 69.9 ms as two kernels
+// with row sums).
+UpdLaunch upd_launch(const ma_ctx *h) {
+  const bool csu = h->csu_ok && !(h->flags & MA_FLAG_ROW_SUMS);
+  const bool fcsu = csu && h->fused_csu_ok && !h->fused_ok;
+  return UpdLaunch{csu, csu ? h->csu_lds : h->apply_lds, fcsu, h->fused_csu_lds};
+}
+
 ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float decay) {
   ApplyArgs a{};
   a.G = h->window;
@@ -452,6 +513,8 @@ ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float 
   a.tm = (int32_t)(t % h->m);
   a.cap = h->cap;
   a.ent_cap = h->ent_cap;
+  a.csu_slots = h->csu_slots;
+  a.fused_union_words = h->fused_union_words;
   a.c1 = c1;
   a.c2 = c2;
   a.lr = h->lr;
@@ -533,6 +596,28 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
   // rows take no space at any m)
   h->fused_ok = h->cpt <= 4 && B_d == h->cpt * kChunkSpan && (int64_t)m * ((kb_max + 63) & ~63LL) <= kFusedEnt &&
                 2 * (int64_t)m <= kFusedBeta;
+  // column-sorted update: every thread holds at most kCsuPerThread of the
+  // block's m * k_b entries, its LDS (bitmap, slot bases, decay factors, a
+  // word per slot and per entry) within the budget, keys of row << 16
+  const int64_t csu_slots = std::min<int64_t>((int64_t)B_d, ents);
+  h->csu_lds = 4 * (2 * (size_t)W + 2 * (size_t)m + (size_t)csu_slots + (size_t)ents);
+  h->csu_ok = ents <= (int64_t)kThreads * kCsuPerThread && h->csu_lds <= kApplyLdsLimit && m <= 65535;
+  h->csu_slots = (int32_t)csu_slots;
+  // the fused kernel with the column-sorted update: one LDS buffer for the
+  // compressor (CompressSmem + staging) and then the update, plus the new
+  // window row; within a third of a CU's LDS
+  {
+    size_t comp_words = 0;
+    switch (h->cpt) {
+      case 1: comp_words = ((sizeof(CompressSmem<1>) + 15) / 16) * 4 + sizeof(FullBlockStage<1>) / 4; break;
+      case 2: comp_words = ((sizeof(CompressSmem<2>) + 15) / 16) * 4 + sizeof(FullBlockStage<2>) / 4; break;
+      default: comp_words = ((sizeof(CompressSmem<4>) + 15) / 16) * 4 + sizeof(FullBlockStage<4>) / 4; break;
+    }
+    const size_t union_words = std::max(comp_words, h->csu_lds / 4);
+    h->fused_union_words = (int32_t)union_words;
+    h->fused_csu_lds = 4 * (union_words + (size_t)kb_max);
+    h->fused_csu_ok = h->csu_ok && h->cpt <= 4 && B_d == h->cpt * kChunkSpan && h->fused_csu_lds <= kFusedCsuLdsLimit;
+  }
   h->chunks = h->n_b >= 8192 ? 8 : 1;
 
   h->codes_bytes = (size_t)((d + 1) / 2);
@@ -610,7 +695,8 @@ int ma_set_step(ma_ctx *h, int64_t t) {
 int ma_set_flags(ma_ctx *h, uint32_t flags) {
   clear_error();
   if (!h) return fail(MA_EINVAL, "ma_set_flags: null handle");
-  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE | MA_FLAG_UNFUSED | MA_FLAG_GLOBAL_QUANT))
+  if (flags & ~(MA_FLAG_NO_EF | MA_FLAG_FORCE_DENSE | MA_FLAG_FORCE_SPARSE | MA_FLAG_UNFUSED | MA_FLAG_GLOBAL_QUANT |
+                MA_FLAG_ROW_SUMS))
     return fail(MA_EINVAL, "ma_set_flags: unknown flag bits");
   h->flags = flags;
   return MA_OK;
@@ -656,6 +742,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   const float c1 = (float)((1.0 - b1) / (1.0 - std::pow(b1, (double)t)));
   const float c2 = (float)((1.0 - b2) / (1.0 - std::pow(b2, (double)t)));
   const float decay = (float)(1.0 - (double)h->lr * (double)h->wd);
+  const UpdLaunch ul = upd_launch(h);
 
   CompressArgs ca{};
   ca.g = grads;
@@ -717,9 +804,9 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     // the block's window, which the first pass completes), then the second
     // pass alone.  Neither writes what the other reads.  The dense update
     // (decoupled decay) is fused for 16-byte aligned parameters.
-    if (h->fused_ok && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
+    if ((ul.fused_csu || h->fused_ok) && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
       if (t0) (void)hipEventRecord(t0, stream);
-      e = dispatch_fused_global1(h->cpt, bf, ca, aa, mode, p_al, h->n_b, n_full, h->apply_lds, stream);
+      e = dispatch_fused_global1(h->cpt, bf, ca, aa, mode, p_al, h->n_b, n_full, ul, stream);
       if (t1) (void)hipEventRecord(t1, stream);
       if (e == hipSuccess) {
         if (t2) (void)hipEventRecord(t2, stream);
@@ -741,7 +828,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     if (noalloc) {
       // everything on the caller's stream: pass 1, the update, pass 2
       e = dispatch_global_p1(h->cpt, g_al, ca, h->n_b, n_full, stream);
-      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, stream, bf);
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, ul, stream, bf);
       if (e == hipSuccess) e = dispatch_global_p2(h->cpt, g_al, ca, 0, h->n_b, n_full, stream);
       if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
       h->t = t;
@@ -756,7 +843,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
     if (e == hipSuccess) {
       if (t4) (void)hipEventRecord(t4, h->side);
-      e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, h->apply_lds, h->side, bf);
+      e = dispatch_apply(h->cpt, mode, p_al, aa, h->n_b, ul, h->side, bf);
       if (t5) (void)hipEventRecord(t5, h->side);
     }
     if (e == hipSuccess) {
@@ -784,14 +871,14 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   // Fused path: every full block runs compress and update in one workgroup;
   // a partial last block (if any) runs the two kernels after it.  The dense
   // update (decoupled decay) is fused for 16-byte aligned parameters.
-  if (h->fused_ok && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
+  if ((ul.fused_csu || h->fused_ok) && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
     hipEvent_t tf[2] = {};
     if (timing && !take_events(h, tf, 2)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     hipEvent_t t0 = tf[0], t1 = tf[1];
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, 1);
     e = hipGetLastError();
     if (t0) (void)hipEventRecord(t0, stream);
-    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, mode == kModeDense, ca, aa, n_full, h->apply_lds, stream, bf);
+    if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, mode == kModeDense, p_al, ca, aa, n_full, ul, stream, bf);
     if (t1) {
       (void)hipEventRecord(t1, stream);
       h->events.push_back({2, t0, t1});
@@ -800,7 +887,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
       e = dispatch_compress(h->cpt, g_al, ef, ca, n_full, h->n_b, n_full, stream);
       ApplyArgs at = aa;
       at.first_block = n_full;
-      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, h->apply_lds, stream, bf);
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, ul, stream, bf);
     }
     if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
     h->t = t;
@@ -847,7 +934,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
     aai.first_block = b0;
     hipEvent_t u0 = tp.empty() ? nullptr : tp[4 * (size_t)i + 2], u1 = tp.empty() ? nullptr : tp[4 * (size_t)i + 3];
     if (u0) (void)hipEventRecord(u0, upd);
-    e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, h->apply_lds, upd, bf);
+    e = dispatch_apply(h->cpt, mode, p_al, aai, b1 - b0, ul, upd, bf);
     if (u1) {
       (void)hipEventRecord(u1, upd);
       h->events.push_back({1, u0, u1});
@@ -1016,7 +1103,7 @@ int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *m
   a.mhat = mhat_out;
   a.vhat = vhat_out;
   a.blocks = dblocks;
-  if (e == hipSuccess) e = dispatch_apply(h->cpt, kModeMoments, false, a, nblocks, h->apply_lds, stream);
+  if (e == hipSuccess) e = dispatch_apply(h->cpt, kModeMoments, false, a, nblocks, upd_launch(h), stream);
   // the block list must outlive the kernel
   const hipError_t e2 = hipStreamSynchronize(stream);
   (void)hipFree(dblocks);

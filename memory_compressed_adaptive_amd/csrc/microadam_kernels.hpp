@@ -964,6 +964,8 @@ struct ApplyArgs {
   int64_t first_block;      // MODE 0, 1: blocks first_block .. first_block + grid - 1
   int32_t B, m, tm, cap;    // tm = t mod m; cap = LDS slots per pass
   int32_t ent_cap;          // window entries the LDS copy holds (m*k_b must fit to use it)
+  int32_t csu_slots;        // column-sorted update: slot words (min(B_d, m * max k_b))
+  int32_t fused_union_words;  // step_csu_kernel: LDS words shared by its two phases
   float c1, c2, lr, eps, decay;
 };
 
@@ -1371,6 +1373,361 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
     atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
 }
 
+// ------------------------------------------------------------------ column-sorted update
+
+// The update of one block with its window transposed into columns, one per
+// touched position.  A counting sort by slot in LDS (count with atomics,
+// prefix in slot order, scatter) puts each window entry into its position's
+// column as the key row << 16 | bf16 bits of V; each column (a few entries) is
+// then sorted by row in place and summed by one thread in physical row order,
+// z1 += beta1^r V and z2 += beta2^r V^2 in fp32: the same operations in the
+// same order as adding the rows one at a time, with six barriers per block
+// instead of one per row.  The parameters are then read and written in
+// coalesced 16-byte groups: only 32-byte sectors holding a touched position,
+// or every sector with decoupled decay.
+//
+// LDS (dynamic, CsuSmem): the bitmap and slot bases (W words each), the 2m
+// decay factors, one word per slot (count, then column start / end, then the
+// slot's update value) and one word per entry (first the staged raw window
+// entries, then the column keys).  A thread holds at most kCsuPerThread
+// entries and slots, so the block's m * k_b must not exceed
+// kThreads * kCsuPerThread (the host checks it).
+constexpr int kCsuPerThread = 12;
+
+struct CsuSmem {
+  uint32_t *bits, *wbase;
+  float *beta;
+  uint32_t *slot;   // [min(B_d, m * k_b)]
+  uint32_t *col;    // [m * k_b]
+  uint32_t *cnt;    // kWaves + 1 words (scans)
+};
+
+template <int CPT>
+__device__ __forceinline__ CsuSmem csu_smem(const ApplyArgs &A, uint32_t *smem, uint32_t *cnt) {
+  constexpr int W = CPT * kChunkSpan / 32;
+  CsuSmem sm;
+  sm.bits = smem;
+  sm.wbase = smem + W;
+  sm.beta = reinterpret_cast<float *>(smem + 2 * W);
+  sm.slot = smem + 2 * W + 2 * A.m;
+  sm.col = sm.slot + A.csu_slots;
+  sm.cnt = cnt;
+  return sm;
+}
+
+// Row of flat entry x = i * kb + q for x < 2^16: floor((x + 1/2) / kb) in
+// fp32 is exact (the error of the product, below 2^-7 / kb, is far from the
+// distance 1 / (2 kb) to an integer).
+__device__ __forceinline__ int csu_row(int x, float inv_kb) {
+  return (int)(((float)x + 0.5f) * inv_kb);
+}
+
+// MODE as apply_block (kModeSparse, kModeDense, kModeMoments).
+// newrow (optional): window row t mod m of the block, already in LDS (the
+// fused kernel's compressor wrote it there beside its global copy); that row
+// is then copied from LDS instead of read from global memory.  pre_kb >= 0:
+// the block's window offset and quota, already known (re-reading them from
+// global memory would wait for all the vector memory in flight, the
+// compressor's stores included).
+// EARLY: the parameters' loads are issued before the column sums (their
+// latency overlaps them; 4 words per load held meanwhile), else after them
+// (the fused kernel, whose registers are taken by the compressor's budget).
+template <int CPT, int MODE, bool ALIGNED, bool BF = false, bool EARLY = true>
+__device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, int64_t out_row, const CsuSmem &sm,
+                                                const uint32_t *newrow = nullptr, int64_t pre_off = 0,
+                                                int pre_kb = -1) {
+  constexpr int W = CPT * kChunkSpan / 32;           // bitmap words
+  constexpr int WPT = (W + kThreads - 1) / kThreads; // words a thread owns
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  __builtin_assume(tid >= 0 && tid < kThreads);
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t s = j * (int64_t)A.B;
+  const int L = (int)((A.d - s) < (int64_t)A.B ? (A.d - s) : (int64_t)A.B);
+  const int64_t off = pre_kb >= 0 ? pre_off : A.off_tab[j];
+  const int kb = pre_kb >= 0 ? pre_kb : (int)(A.off_tab[j + 1] - off);
+  const int M = A.m;
+  const int E = M * kb;
+  const float inv_kb = kb > 0 ? 1.0f / (float)kb : 0.f;
+
+  // ---------------- the block's m * k_b window entries into LDS (col), the
+  // decay factors, a cleared bitmap
+  for (int w = tid; w < W; w += kThreads) sm.bits[w] = 0u;
+  stage_beta(A, sm.beta, tid);
+  for (int x0 = wv * 64; x0 < E; x0 += kThreads) {
+    const int x = x0 + lane;
+    if (x < E) {
+      const int i = csu_row(x, inv_kb), q = x - i * kb;
+      if (!newrow || i != A.tm)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.G + (int64_t)i * A.k + off + q),
+                                         (lds_void_t *)(&sm.col[x0]), 4, 0, kCacheStream);
+    }
+  }
+  if (newrow)
+    for (int q = tid; q < kb; q += kThreads) sm.col[A.tm * kb + q] = newrow[q];
+  wait_vm_all();
+  __syncthreads();
+
+  // ---------------- each thread's entries (x = tid + u * 512) into registers,
+  // and the bitmap of the touched positions.  A zero value adds nothing
+  // (unwritten rows are all zero); an index outside the block (only possible
+  // in an imported state) is ignored.
+  uint32_t ent[kCsuPerThread];
+#pragma unroll
+  for (int u = 0; u < kCsuPerThread; ++u) {
+    const int x = tid + u * kThreads;
+    uint32_t e = (x < E) ? sm.col[x] : 0u;
+    if (!(e & 0x7fff0000u) || (int)(e & 0xffffu) >= L) e = 0u;
+    ent[u] = e;
+    if (e) atomicOr(&sm.bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+  }
+  __syncthreads();
+
+  // ---------------- compact slots: slot(p) = number of touched positions below p
+  uint32_t wc[WPT], mine = 0;
+#pragma unroll
+  for (int r = 0; r < WPT; ++r) {
+    const int w = tid * WPT + r;
+    wc[r] = (w < W) ? (uint32_t)__popc(sm.bits[w]) : 0u;
+    mine += wc[r];
+  }
+  uint32_t cnt1[1] = {mine}, pos1[1], U;
+  ordered_offsets<1>(cnt1, pos1, U, sm.cnt);
+  {
+    uint32_t b = pos1[0];
+#pragma unroll
+    for (int r = 0; r < WPT; ++r) {
+      const int w = tid * WPT + r;
+      if (w < W) sm.wbase[w] = b;
+      b += wc[r];
+    }
+  }
+  for (uint32_t x = (uint32_t)tid; x < U; x += kThreads) sm.slot[x] = 0u;
+  __syncthreads();
+
+  // ---------------- counting sort by slot: counts ...
+  uint32_t sl[kCsuPerThread];
+#pragma unroll
+  for (int u = 0; u < kCsuPerThread; ++u) {
+    const uint32_t e = ent[u], I = e & 0xffffu;
+    sl[u] = e ? sm.wbase[I >> 5] + (uint32_t)__popc(sm.bits[I >> 5] & ((1u << (I & 31u)) - 1u)) : 0xffffffffu;
+    if (e) atomicAdd(&sm.slot[sl[u]], 1u);
+  }
+  __syncthreads();
+  // ... column starts, an exclusive prefix in slot order (a thread's words
+  // hold a contiguous run of slots) ...
+  const int w0 = tid * WPT;
+  const uint32_t s_lo = (w0 < W) ? sm.wbase[w0] : U;
+  const uint32_t s_hi = (w0 + WPT < W) ? sm.wbase[w0 + WPT] : U;
+  uint32_t csum = 0;
+  for (uint32_t x = s_lo; x < s_hi; ++x) csum += sm.slot[x];
+  {
+    uint32_t c1v[1] = {csum}, p1v[1], tot;
+    ordered_offsets<1>(c1v, p1v, tot, sm.cnt);
+    uint32_t run = p1v[0];
+    for (uint32_t x = s_lo; x < s_hi; ++x) {
+      const uint32_t c = sm.slot[x];
+      sm.slot[x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // ... scatter of the keys (row << 16 | V bits): slot[s] ends at the column's end
+#pragma unroll
+  for (int u = 0; u < kCsuPerThread; ++u) {
+    if (ent[u]) {
+      const uint32_t p = atomicAdd(&sm.slot[sl[u]], 1u);
+      sm.col[p] = ((uint32_t)csu_row(tid + u * kThreads, inv_kb) << 16) | (ent[u] >> 16);
+    }
+  }
+  __syncthreads();
+
+  // ---------------- the parameters' loads, all issued at once (before the
+  // column sums with EARLY, so that their latency overlaps them).  Consecutive
+  // threads take consecutive 16-byte groups (4 fp32 or 8 bf16 parameters):
+  // every access is coalesced across the wave.  In the sparse mode (decay
+  // exactly 1) only the 32-byte sectors holding a touched position are read
+  // and written, both of their groups whole.
+  constexpr int G = BF ? 8 : 4;                      // parameters per 16-byte group
+  constexpr int SEC = BF ? 16 : 8;                   // parameters per 32-byte sector
+  constexpr int NG = CPT * kChunkSpan / G;           // groups per block
+  constexpr int NIT = NG / kThreads;                 // groups per thread
+  // every group whole and aligned (uniform over the block): 16-byte loads and
+  // stores; otherwise element by element at the end
+  const bool vec_all = ALIGNED && (L % G) == 0;
+  u32x4 raw[MODE == kModeMoments ? 1 : NIT];
+  uint32_t want = 0;                                 // bit it: group it is read and written
+  auto issue_loads = [&]() {
+    if (MODE != kModeMoments) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i0 = (it * kThreads + tid) * G;
+        raw[it] = u32x4{0u, 0u, 0u, 0u};
+        if (i0 >= L) continue;
+        const uint32_t word = sm.bits[i0 >> 5];
+        const uint32_t sbits = (word >> (i0 & 31 & ~(SEC - 1))) & (SEC == 32 ? 0xffffffffu : ((1u << SEC) - 1u));
+        if (MODE == kModeSparse && !sbits) continue;
+        want |= 1u << it;
+        if (vec_all)
+          raw[it] = BF ? *reinterpret_cast<const u32x4 *>(A.theta16 + s + i0)
+                       : *reinterpret_cast<const u32x4 *>(A.theta + s + i0);
+      }
+    }
+  };
+  if (EARLY) issue_loads();
+
+  // ---------------- each slot's column: sorted by row, summed in row order
+  // (slots tid, tid + 512, ...; their start and end are read before any slot
+  // word is overwritten with its update value)
+  uint32_t cst[kCsuPerThread], cen[kCsuPerThread];
+#pragma unroll
+  for (int u = 0; u < kCsuPerThread; ++u) {
+    const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+    cst[u] = (x < U && x > 0) ? sm.slot[x - 1] : 0u;
+    cen[u] = (x < U) ? sm.slot[x] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kCsuPerThread; ++u) {
+    const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+    if (x < U) {
+      const uint32_t c0 = cst[u], c1 = cen[u];
+      for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
+        const uint32_t key = sm.col[a];
+        uint32_t b = a;
+        while (b > c0 && sm.col[b - 1] > key) {
+          sm.col[b] = sm.col[b - 1];
+          --b;
+        }
+        sm.col[b] = key;
+      }
+      float z1 = 0.f, z2 = 0.f;
+      for (uint32_t a = c0; a < c1; ++a) {
+        const uint32_t key = sm.col[a];
+        int r = A.tm - (int)(key >> 16);
+        if (r < 0) r += M;
+        const float V = bf16_bits_to_f32(key & 0xffffu);
+        z1 = z1 + decay_factor(sm.beta, r) * V;
+        z2 = z2 + decay_factor(sm.beta, M + r) * (V * V);
+      }
+      const float mh = A.c1 * z1;
+      const float vh = A.c2 * z2;
+      if (MODE == kModeMoments) {
+        // the slot's position: its word by binary search over the slot
+        // bases, then the matching set bit
+        int lo = 0, hi = W - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.wbase[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        uint32_t bits = sm.bits[lo];
+        for (uint32_t n = x - sm.wbase[lo]; n > 0; --n) bits &= bits - 1u;
+        const int p = lo * 32 + __ffs(bits) - 1;
+        A.mhat[out_row * A.B + p] = mh;
+        A.vhat[out_row * A.B + p] = vh;
+      } else {
+        sm.slot[x] = f2u(A.lr * (mh / (sqrtf(vh) + A.eps)));
+      }
+    }
+  }
+  if (MODE == kModeMoments) {
+    // positions without an entry: 0
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int e = 0; e < kChunk; ++e) {
+        const int i = c * kChunkSpan + tid * kChunk + e;
+        if (i < L && !((sm.bits[i >> 5] >> (i & 31)) & 1u)) {
+          A.mhat[out_row * A.B + i] = 0.f;
+          A.vhat[out_row * A.B + i] = 0.f;
+        }
+      }
+    return;
+  }
+  __syncthreads();
+
+  // ---------------- parameters: theta = theta * decay - update on touched positions
+  if (!EARLY) issue_loads();
+  if (MODE != kModeMoments && vec_all) {
+    // no loads here: the stores need no waits
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (!((want >> it) & 1u)) continue;
+      const int i0 = (it * kThreads + tid) * G;
+      const int w = i0 >> 5;
+      const uint32_t word = sm.bits[w];
+      const uint32_t gb = (word >> (i0 & 31)) & ((1u << G) - 1u);   // this group's touched bits
+      const uint32_t base = sm.wbase[w] + (uint32_t)__popc(word & ((1u << (i0 & 31)) - 1u));
+      float th[G];
+      const uint32_t vv[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+      for (int e = 0; e < G; ++e)
+        th[e] = BF ? ((e & 1) ? u2f(vv[e >> 1] & 0xffff0000u) : u2f(vv[e >> 1] << 16)) : u2f(vv[e]);
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        if (MODE == kModeDense) th[e] = th[e] * A.decay;
+        if ((gb >> e) & 1u) th[e] = th[e] - u2f(sm.slot[base + (uint32_t)__popc(gb & ((1u << e) - 1u))]);
+      }
+      if (BF) {
+        u32x4 v;
+        v.x = f32_to_bf16_rne(th[0]) | (f32_to_bf16_rne(th[1]) << 16);
+        v.y = f32_to_bf16_rne(th[2]) | (f32_to_bf16_rne(th[3]) << 16);
+        v.z = f32_to_bf16_rne(th[4]) | (f32_to_bf16_rne(th[5]) << 16);
+        v.w = f32_to_bf16_rne(th[6]) | (f32_to_bf16_rne(th[7]) << 16);
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(A.theta16 + s + i0));
+      } else {
+        const u32x4 v0 = {f2u(th[0]), f2u(th[1]), f2u(th[2]), f2u(th[3])};
+        __builtin_nontemporal_store(v0, reinterpret_cast<u32x4 *>(A.theta + s + i0));
+      }
+    }
+  } else if (MODE != kModeMoments) {
+    // unaligned parameters or a partial group: element by element
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (!((want >> it) & 1u)) continue;
+      const int i0 = (it * kThreads + tid) * G;
+      const int w = i0 >> 5;
+      const uint32_t word = sm.bits[w];
+      const uint32_t gb = (word >> (i0 & 31)) & ((1u << G) - 1u);
+      const uint32_t base = sm.wbase[w] + (uint32_t)__popc(word & ((1u << (i0 & 31)) - 1u));
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        if (i0 + e < L && (MODE == kModeDense || ((gb >> e) & 1u))) {
+          float th = ld_param<BF>(A, s + i0 + e);
+          if (MODE == kModeDense) th = th * A.decay;
+          if ((gb >> e) & 1u) th = th - u2f(sm.slot[base + (uint32_t)__popc(gb & ((1u << e) - 1u))]);
+          st_param<BF>(A, s + i0 + e, th);
+        }
+      }
+    }
+  }
+  if (A.touched && tid == 0) atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
+}
+
+// One workgroup per block (blocks first_block .. first_block + grid - 1, or
+// the listed ones in MODE 2), column-sorted update.
+template <int CPT, int MODE, bool ALIGNED, bool BF = false>
+__global__ __launch_bounds__(kThreads) void apply_csu_kernel(ApplyArgs A) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t s_cnt[kWaves + 1];
+  const int64_t j = (MODE == kModeMoments) ? A.blocks[blockIdx.x]
+                                           : A.first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  apply_block_csu<CPT, MODE, ALIGNED, BF>(A, j, (int64_t)blockIdx.x, csu_smem<CPT>(A, smem, s_cnt));
+}
+
+// The column-sorted update of the blocks in the device list A.blocks[0 .. *A.n_list).
+template <int CPT, bool BF = false, int MODE = kModeSparse>
+__global__ __launch_bounds__(kThreads) void apply_csu_list_kernel(ApplyArgs A) {
+  extern __shared__ uint32_t smem[];
+  __shared__ uint32_t s_cnt[kWaves + 1];
+  const unsigned int n = *A.n_list;
+  for (unsigned int q = blockIdx.x; q < n; q += gridDim.x) {
+    apply_block_csu<CPT, MODE, false, BF>(A, A.blocks[q], 0, csu_smem<CPT>(A, smem, s_cnt));
+    __syncthreads();
+  }
+}
+
 // LDS of the standalone update: dynamic, laid out as in ApplySmem.
 template <int CPT>
 __device__ __forceinline__ ApplySmem apply_smem(const ApplyArgs &A, uint32_t *smem, uint32_t *cnt, int64_t j) {
@@ -1433,7 +1790,8 @@ constexpr int kFusedEnt = 1984;
 // global quantizer's first pass (selection, window row, the block's min / max
 // and cut) with the update; the codes are left to the second pass.  MODE:
 // the update's mode (kModeDense with decoupled decay), PAL: 16-byte aligned
-// parameters (required by the dense mode here).
+// parameters (required by the dense mode here; in the sparse mode only the
+// column-sorted update uses it).
 template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(CompressArgs C, ApplyArgs A,
                                                                              int64_t first_block) {
@@ -1499,6 +1857,46 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   as.off = in.off;
   as.kb = in.kb;
   apply_block<CPT, MODE, PAL, true, BF>(A, j, 0, as);
+}
+
+// The whole step of one full, aligned block in one workgroup with the
+// column-sorted update: the compressor (rows a1-a5), then the update (a6-a7)
+// reading the block's m window rows after the compressor has finished.  One
+// static LDS buffer of kFusedCsuWords (a third of a CU's LDS: three
+// workgroups per CU) serves both phases, the compressor's CompressSmem and
+// staging first and the update's CsuSmem after (A.fused_union_words words);
+// the new window row is kept apart, behind it, where the compressor writes it
+// beside its global copy.  Co-resident workgroups are in different phases, so
+// the arithmetic-bound compressor and the memory-bound update share each CU.
+// Blocks the compressor defers are left to compress_deferred_kernel and
+// apply_csu_list_kernel, as in step_full_kernel.
+// (A static buffer: with a dynamic one the compressor's addresses are formed
+// at run time and its registers spill.)  Three workgroups fit a CU's 160 KiB
+// when each takes at most 53,760 bytes (LDS is allocated in 1,280-byte
+// granules), the scan words included.
+constexpr int kFusedCsuWords = (53760 - 64) / 4;
+
+template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
+__global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_csu_kernel(CompressArgs C, ApplyArgs A,
+                                                                            int64_t first_block) {
+  static_assert(QMODE == kQBlock || (QMODE == kQGlobal1 && EF), "the fused kernel runs a step or a first pass");
+  static_assert(MODE == kModeSparse || (MODE == kModeDense && PAL), "dense updates in the fused kernel are aligned");
+  static_assert(sizeof(FullBlockStage<CPT>) >= 4u * (CPT * kChunkSpan / 2), "the random words fit the staging space");
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kFusedCsuWords];
+  __shared__ uint32_t s_cnt[kWaves + 1];
+  constexpr int kSmWords = (int)((sizeof(CompressSmem<CPT>) + 15) / 16 * 4);
+  CompressSmem<CPT> &sm = *reinterpret_cast<CompressSmem<CPT> *>(lds);
+  FullBlockStage<CPT> *st = reinterpret_cast<FullBlockStage<CPT> *>(lds + kSmWords);
+  uint32_t *newrow = lds + A.fused_union_words;
+  const int64_t j = first_block + xcd_block((int64_t)blockIdx.x, (int64_t)gridDim.x);
+  FullBlockInputs<CPT> in;
+  stage_full_block<CPT, EF>(C, j, *st, in);
+  const bool done = compress_block<CPT, true, true, EF, true, QMODE>(C, sm, j, j * (int64_t)C.B, CPT * kChunkSpan,
+                                                                   in.off, in.kb, st, &in, newrow,
+                                                                   reinterpret_cast<uint32_t *>(st), nullptr);
+  if (!done) return;
+  __syncthreads();
+  apply_block_csu<CPT, MODE, PAL, BF, false>(A, j, 0, csu_smem<CPT>(A, lds, s_cnt), newrow, in.off, in.kb);
 }
 
 }  // namespace microadam

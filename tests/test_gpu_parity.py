@@ -212,6 +212,8 @@ def test_global_quantizer_single_block_equals_block_mode():
     (100_003, 16384, 1000, 4, 0.0, L.MA_FLAG_GLOBAL_QUANT, False),  # one (delta, Delta) over all d
     (100_003, 16384, 1000, 4, 0.1, L.MA_FLAG_GLOBAL_QUANT, False),  # the same with decay (dense, fused)
     (60_000, 16384, 6000, 37, 0.0, 0, False),                  # window too large for LDS: rows from HBM
+    (5 * 16384 + 9, 16384, (5 * 16384 + 9) // 100, 20, 0.0, 0, False),   # fused column-sorted update
+    (5 * 16384 + 9, 16384, (5 * 16384 + 9) // 100, 20, 0.1, 0, False),   # the same with decay
 ])
 def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
     # ma_step_bf16: widen, fp32 step, round to nearest even once
@@ -230,7 +232,7 @@ def test_bf16_parameters(d, B, k, m, wd, flags, misalign):
         th_gpu = torch.empty(d, dtype=torch.int16, device="cuda")
     th_gpu.copy_(torch.from_numpy(th16.view(np.int16)))
     changed = 0
-    for t in range(1, 6):
+    for t in range(1, max(6, m + 3)):
         g = gauss_grads(rng, d, t)
         say(f"[bf16 params] step {t}: d={d} B={B} m={m} wd={wd} flags={flags} misalign={misalign}")
         opt.step(th_gpu, to_gpu_bf16(g))
@@ -535,6 +537,69 @@ def test_nonfinite_gradients(B, flags, gq, wd):
     full_parity(f"non-finite B={B} flags={flags} global={gq} wd={wd}", d, B, d // 100, 4, 5,
                 lr=1e-2 if wd else 1e-4, wd=wd, flags=oflags, gpu_only_flags=flags & ~L.MA_FLAG_NO_EF,
                 grad_fn=_nonfinite_grads(B), global_quant=gq)
+
+
+# ---------------------------------------------------------------- the two update algorithms
+
+@pytest.mark.parametrize("d,B,k,m,wd,flags", [
+    (200_003, 16384, 2000, 4, 0.0, L.MA_FLAG_UNFUSED),        # sparse update, ragged block
+    (200_003, 16384, 2000, 4, 0.1, L.MA_FLAG_UNFUSED),        # dense update (decay)
+    (60_000, 16384, 6000, 37, 0.0, 0),                        # m * k_b beyond the column-sorted update's LDS
+    (4 * 16384 + 99, 16384, (4 * 16384 + 99) // 100, 37, 0.0, 0),  # m = 37 at k = d/100: several slot passes
+    (20_011, 1003, 500, 4, 0.0, L.MA_FLAG_UNFUSED),           # odd B_d
+])
+@pytest.mark.parametrize("row_sums", [False, True])
+def test_update_algorithms(d, B, k, m, wd, flags, row_sums):
+    # the column-sorted update (default) and the row-by-row sums
+    # (MA_FLAG_ROW_SUMS) against the oracle, with the moments
+    full_parity(f"update row_sums={row_sums} d={d} m={m} wd={wd}", d, B, k, m, m + 3, lr=1e-2 if wd else 1e-4,
+                wd=wd, gpu_only_flags=flags | (L.MA_FLAG_ROW_SUMS if row_sums else 0))
+
+
+@pytest.mark.parametrize("label,wd,flags,gq,grad_fn,misalign", [
+    ("plain", 0.0, 0, False, None, False),
+    ("decay", 0.1, 0, False, None, False),                 # dense update, 16-byte groups
+    ("global", 0.0, 0, True, None, False),                 # first pass fused with the update
+    ("global decay", 0.1, 0, True, None, False),
+    ("no EF", 0.0, L.MA_FLAG_NO_EF, False, None, False),
+    ("deferred", 0.0, 0, False, "tied", False),            # tie-heavy blocks: the column-sorted list kernel
+])
+def test_fused_column_sorted_update(label, wd, flags, gq, grad_fn, misalign):
+    # m = 20 at k = d/100: the window does not fit step_full_kernel's LDS, so
+    # full blocks run step_csu_kernel (compressor and column-sorted update in
+    # one workgroup); the ragged last block runs the two kernels
+    def tied(rng, d, t):
+        g = gauss_grads(rng, d, t)
+        g[16384:3 * 16384] = O.bf16_rne(np.full(2 * 16384, 1e-3, np.float32))
+        return g
+    d = 6 * 16384 + 777
+    full_parity(f"fused csu {label}", d, 16384, d // 100, 20, 23, lr=1e-2 if wd else 1e-4, wd=wd,
+                flags=flags & O.FLAG_NO_EF, global_quant=gq, grad_fn=tied if grad_fn == "tied" else None,
+                misalign=misalign, moments=True)
+
+
+def test_fused_column_sorted_update_unaligned_parameters():
+    # parameters 4 bytes off a 16-byte boundary: the sparse update element by element
+    d, m = 5 * 16384, 20
+    k = d // 100
+    rng = np.random.default_rng(13)
+    theta0 = (rng.standard_normal(d) * 0.02).astype(np.float32)
+    opt = MicroAdam(d, 16384, k, m)
+    orc = O.FullState(O.make_cfg(d, 16384, k, m))
+    buf = torch.empty(d + 1, dtype=torch.float32, device="cuda")
+    th_gpu = buf[1:]
+    th_gpu.copy_(torch.from_numpy(theta0))
+    th_cpu = theta0.copy()
+    for t in range(1, m + 4):
+        g = gauss_grads(rng, d, t)
+        say(f"[fused csu unaligned params] step {t}")
+        prev_gpu, prev_cpu = th_gpu.cpu().numpy(), th_cpu.copy()
+        opt.step(th_gpu, to_gpu_bf16(g))
+        torch.cuda.synchronize()
+        orc.step(th_cpu, g)
+        assert_bits_equal(f"unaligned t={t} window", opt.window(), orc.G)
+        assert_bits_equal(f"unaligned t={t} codes", opt.codes_bytes(), orc.ef)
+        assert check_theta(f"unaligned t={t} theta", th_gpu.cpu().numpy(), th_cpu, prev_gpu, prev_cpu) == 0
 
 
 # ---------------------------------------------------------------- limits
