@@ -91,11 +91,16 @@ __device__ __forceinline__ uint32_t philox_block_key(uint64_t seed, int64_t t, i
 // pcg_hash of Jarzynski and Olano (JCGT 2020): a PCG-32 LCG step followed by
 // the RXS-M-XS output permutation.  One call gives the 16-bit uniforms of two
 // neighbouring elements (low half: even element, high half: odd element).
-__device__ __forceinline__ uint32_t pcg_hash(uint32_t x) {
-  const uint32_t st = x * 747796405u + 2891336453u;
+// pcg_out is its output permutation of the LCG state st: hashes of counters
+// x and x + n have states n * 747796405 apart (mod 2^32), so a run of
+// counters steps the state by an addition instead of a multiplication.
+constexpr uint32_t kPcgMul = 747796405u;
+__device__ __forceinline__ uint32_t pcg_out(uint32_t st) {
   const uint32_t w = ((st >> ((st >> 28u) + 4u)) ^ st) * 277803737u;
   return (w >> 22u) ^ w;
 }
+__device__ __forceinline__ uint32_t pcg_state(uint32_t x) { return x * kPcgMul + 2891336453u; }
+__device__ __forceinline__ uint32_t pcg_hash(uint32_t x) { return pcg_out(pcg_state(x)); }
 
 // Top-k keys.  The key of a value is the 31-bit pattern of |x|: for finite
 // values that is the order of |x|, +-Inf is above every finite value and NaN
@@ -617,8 +622,9 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
           // bitmap of the window's other rows
           const int t7 = tid - 64;
           if (EF && QMODE == kQBlock && lds_hash) {
-            const uint32_t bkey = philox_block_key(A.seed, A.t, j);
-            for (int p = t7; p < L / 2; p += kThreads - 64) lds_hash[p] = pcg_hash(bkey + (uint32_t)p);
+            constexpr int kStride = kThreads - 64;
+            uint32_t st = pcg_state(philox_block_key(A.seed, A.t, j) + (uint32_t)t7);
+            for (int p = t7; p < L / 2; p += kStride, st += (uint32_t)kStride * kPcgMul) lds_hash[p] = pcg_out(st);
           }
           if (fb) {
             for (int i = 0; i < fb->M; ++i) {
@@ -826,7 +832,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       }
 #pragma unroll
       for (int pr = 0; pr < kChunk / 2; ++pr) {
-        const uint32_t h = (FULL && hashed) ? hw[pr] : pcg_hash(bkey + (uint32_t)((i0 >> 1) + pr));
+        const uint32_t h = (FULL && hashed) ? hw[pr] : pcg_out(pcg_state(bkey + (uint32_t)(i0 >> 1)) + (uint32_t)pr * kPcgMul);
         ev = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr], mn, inv, h & 0xffffu), pr, ev);
         od = __builtin_amdgcn_cvt_pk_u8_f32(quant_code_f(a[c][2 * pr + 1], mn, inv, h >> 16), pr, od);
       }
@@ -1472,14 +1478,20 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   // and the bitmap of the touched positions.  A zero value adds nothing
   // (unwritten rows are all zero); an index outside the block (only possible
   // in an imported state) is ignored.
+  // (entries and slots per thread: nE = ceil(E / 512), uniform, so the
+  // unrolled loops below skip their unused iterations with a scalar branch)
+  const int nE = (E + kThreads - 1) / kThreads;
   uint32_t ent[kCsuPerThread];
 #pragma unroll
   for (int u = 0; u < kCsuPerThread; ++u) {
-    const int x = tid + u * kThreads;
-    uint32_t e = (x < E) ? sm.col[x] : 0u;
-    if (!(e & 0x7fff0000u) || (int)(e & 0xffffu) >= L) e = 0u;
-    ent[u] = e;
-    if (e) atomicOr(&sm.bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+    ent[u] = 0u;
+    if (u < nE) {
+      const int x = tid + u * kThreads;
+      uint32_t e = (x < E) ? sm.col[x] : 0u;
+      if (!(e & 0x7fff0000u) || (int)(e & 0xffffu) >= L) e = 0u;
+      ent[u] = e;
+      if (e) atomicOr(&sm.bits[(e & 0xffffu) >> 5], 1u << (e & 31u));
+    }
   }
   __syncthreads();
 
@@ -1509,9 +1521,12 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   uint32_t sl[kCsuPerThread];
 #pragma unroll
   for (int u = 0; u < kCsuPerThread; ++u) {
-    const uint32_t e = ent[u], I = e & 0xffffu;
-    sl[u] = e ? sm.wbase[I >> 5] + (uint32_t)__popc(sm.bits[I >> 5] & ((1u << (I & 31u)) - 1u)) : 0xffffffffu;
-    if (e) atomicAdd(&sm.slot[sl[u]], 1u);
+    sl[u] = 0xffffffffu;
+    if (u < nE) {
+      const uint32_t e = ent[u], I = e & 0xffffu;
+      sl[u] = e ? sm.wbase[I >> 5] + (uint32_t)__popc(sm.bits[I >> 5] & ((1u << (I & 31u)) - 1u)) : 0xffffffffu;
+      if (e) atomicAdd(&sm.slot[sl[u]], 1u);
+    }
   }
   __syncthreads();
   // ... column starts, an exclusive prefix in slot order (a thread's words
@@ -1521,54 +1536,55 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   const uint32_t s_hi = (w0 + WPT < W) ? sm.wbase[w0 + WPT] : U;
   uint32_t csum = 0;
   for (uint32_t x = s_lo; x < s_hi; ++x) csum += sm.slot[x];
+  // (a slot word is then position << 16 | column start: the thread walks the
+  // set bits of its words, which are its slots in order; E < 2^16)
   {
     uint32_t c1v[1] = {csum}, p1v[1], tot;
     ordered_offsets<1>(c1v, p1v, tot, sm.cnt);
-    uint32_t run = p1v[0];
-    for (uint32_t x = s_lo; x < s_hi; ++x) {
-      const uint32_t c = sm.slot[x];
-      sm.slot[x] = run;
-      run += c;
+    uint32_t run = p1v[0], x = s_lo;
+#pragma unroll
+    for (int r = 0; r < WPT; ++r) {
+      const int w = w0 + r;
+      uint32_t bits = (w < W) ? sm.bits[w] : 0u;
+      while (bits) {
+        const uint32_t c = sm.slot[x];
+        sm.slot[x] = ((uint32_t)(w * 32 + __ffs(bits) - 1) << 16) | run;
+        run += c;
+        ++x;
+        bits &= bits - 1u;
+      }
     }
   }
   __syncthreads();
-  // ... scatter of the keys (row << 16 | V bits): slot[s] ends at the column's end
+  // ... scatter of the keys (row << 16 | V bits): a slot's low half then ends
+  // at the column's end
 #pragma unroll
   for (int u = 0; u < kCsuPerThread; ++u) {
-    if (ent[u]) {
-      const uint32_t p = atomicAdd(&sm.slot[sl[u]], 1u);
+    if (u < nE && ent[u]) {
+      const uint32_t p = atomicAdd(&sm.slot[sl[u]], 1u) & 0xffffu;
       sm.col[p] = ((uint32_t)csu_row(tid + u * kThreads, inv_kb) << 16) | (ent[u] >> 16);
     }
   }
   __syncthreads();
 
-  // ---------------- the parameters' loads, all issued at once (before the
-  // column sums with EARLY, so that their latency overlaps them).  Consecutive
-  // threads take consecutive 16-byte groups (4 fp32 or 8 bf16 parameters):
-  // every access is coalesced across the wave.  In the sparse mode (decay
-  // exactly 1) only the 32-byte sectors holding a touched position are read
-  // and written, both of their groups whole.
+  // ---------------- dense mode: the parameters' loads, all issued at once
+  // (before the column sums with EARLY, so that their latency overlaps them).
+  // Consecutive threads take consecutive 16-byte groups (4 fp32 or 8 bf16
+  // parameters): every access is coalesced across the wave.
   constexpr int G = BF ? 8 : 4;                      // parameters per 16-byte group
-  constexpr int SEC = BF ? 16 : 8;                   // parameters per 32-byte sector
   constexpr int NG = CPT * kChunkSpan / G;           // groups per block
   constexpr int NIT = NG / kThreads;                 // groups per thread
   // every group whole and aligned (uniform over the block): 16-byte loads and
   // stores; otherwise element by element at the end
   const bool vec_all = ALIGNED && (L % G) == 0;
-  u32x4 raw[MODE == kModeMoments ? 1 : NIT];
-  uint32_t want = 0;                                 // bit it: group it is read and written
+  u32x4 raw[MODE == kModeDense ? NIT : 1];
   auto issue_loads = [&]() {
-    if (MODE != kModeMoments) {
+    if (MODE == kModeDense) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int i0 = (it * kThreads + tid) * G;
         raw[it] = u32x4{0u, 0u, 0u, 0u};
-        if (i0 >= L) continue;
-        const uint32_t word = sm.bits[i0 >> 5];
-        const uint32_t sbits = (word >> (i0 & 31 & ~(SEC - 1))) & (SEC == 32 ? 0xffffffffu : ((1u << SEC) - 1u));
-        if (MODE == kModeSparse && !sbits) continue;
-        want |= 1u << it;
-        if (vec_all)
+        if (vec_all && i0 < L)
           raw[it] = BF ? *reinterpret_cast<const u32x4 *>(A.theta16 + s + i0)
                        : *reinterpret_cast<const u32x4 *>(A.theta + s + i0);
       }
@@ -1577,56 +1593,79 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   if (EARLY) issue_loads();
 
   // ---------------- each slot's column: sorted by row, summed in row order
-  // (slots tid, tid + 512, ...; their start and end are read before any slot
-  // word is overwritten with its update value)
-  uint32_t cst[kCsuPerThread], cen[kCsuPerThread];
+  // (slots tid, tid + 512, ...).  Sparse mode: the thread that sums a slot
+  // updates its parameter, whose load it issued first; every lane loads
+  // (lanes past the last slot re-load its parameter) and every loaded value
+  // is used, or the compiler would wait for all vector memory (in the fused
+  // kernel, the compressor's stores included).  Dense mode: the update value
+  // replaces the slot word, so each slot's column start and end are read
+  // first, before a barrier.
+  const int nU = (int)((U + kThreads - 1) / kThreads);   // slots per thread, uniform
+  uint32_t cst[MODE == kModeDense ? kCsuPerThread : 1], cen[MODE == kModeDense ? kCsuPerThread : 1];
+  float thv[MODE == kModeSparse ? kCsuPerThread : 1];
+  if (MODE == kModeDense) {
 #pragma unroll
-  for (int u = 0; u < kCsuPerThread; ++u) {
-    const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
-    cst[u] = (x < U && x > 0) ? sm.slot[x - 1] : 0u;
-    cen[u] = (x < U) ? sm.slot[x] : 0u;
+    for (int u = 0; u < kCsuPerThread; ++u) {
+      cst[u] = cen[u] = 0u;
+      if (u < nU) {
+        const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
+        cst[u] = (x < U && x > 0) ? sm.slot[x - 1] & 0xffffu : 0u;
+        cen[u] = (x < U) ? sm.slot[x] & 0xffffu : 0u;
+      }
+    }
+    __syncthreads();
+  } else if (MODE == kModeSparse) {
+    if (U == 0) return;
+    // (all of them, unconditionally: a scalar branch between a load and its
+    // use makes the compiler wait for all vector memory there)
+#pragma unroll
+    for (int u = 0; u < kCsuPerThread; ++u) {
+      const uint32_t x = min((uint32_t)tid + (uint32_t)(u * kThreads), U - 1u);
+      thv[u] = ld_param<BF>(A, s + (sm.slot[x] >> 16));
+    }
   }
-  __syncthreads();
 #pragma unroll
   for (int u = 0; u < kCsuPerThread; ++u) {
     const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
-    if (x < U) {
-      const uint32_t c0 = cst[u], c1 = cen[u];
-      for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
-        const uint32_t key = sm.col[a];
-        uint32_t b = a;
-        while (b > c0 && sm.col[b - 1] > key) {
-          sm.col[b] = sm.col[b - 1];
-          --b;
-        }
-        sm.col[b] = key;
+    if (MODE == kModeSparse || u < nU) {
+      float th = 0.f;
+      if (MODE == kModeSparse) {
+        th = thv[u];
+        asm volatile("" ::"v"(th));   // the wait for the load, on every path
       }
-      float z1 = 0.f, z2 = 0.f;
-      for (uint32_t a = c0; a < c1; ++a) {
-        const uint32_t key = sm.col[a];
-        int r = A.tm - (int)(key >> 16);
-        if (r < 0) r += M;
-        const float V = bf16_bits_to_f32(key & 0xffffu);
-        z1 = z1 + decay_factor(sm.beta, r) * V;
-        z2 = z2 + decay_factor(sm.beta, M + r) * (V * V);
-      }
-      const float mh = A.c1 * z1;
-      const float vh = A.c2 * z2;
-      if (MODE == kModeMoments) {
-        // the slot's position: its word by binary search over the slot
-        // bases, then the matching set bit
-        int lo = 0, hi = W - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sm.wbase[mid] <= x) lo = mid; else hi = mid - 1;
+      if (x < U) {
+        const uint32_t sx = sm.slot[x];
+        const uint32_t c0 = MODE == kModeDense ? cst[u] : (x > 0 ? sm.slot[x - 1] & 0xffffu : 0u);
+        const uint32_t c1 = MODE == kModeDense ? cen[u] : sx & 0xffffu;
+        for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
+          const uint32_t key = sm.col[a];
+          uint32_t b = a;
+          while (b > c0 && sm.col[b - 1] > key) {
+            sm.col[b] = sm.col[b - 1];
+            --b;
+          }
+          sm.col[b] = key;
         }
-        uint32_t bits = sm.bits[lo];
-        for (uint32_t n = x - sm.wbase[lo]; n > 0; --n) bits &= bits - 1u;
-        const int p = lo * 32 + __ffs(bits) - 1;
-        A.mhat[out_row * A.B + p] = mh;
-        A.vhat[out_row * A.B + p] = vh;
-      } else {
-        sm.slot[x] = f2u(A.lr * (mh / (sqrtf(vh) + A.eps)));
+        float z1 = 0.f, z2 = 0.f;
+        for (uint32_t a = c0; a < c1; ++a) {
+          const uint32_t key = sm.col[a];
+          int r = A.tm - (int)(key >> 16);
+          if (r < 0) r += M;
+          const float V = bf16_bits_to_f32(key & 0xffffu);
+          z1 = z1 + decay_factor(sm.beta, r) * V;
+          z2 = z2 + decay_factor(sm.beta, M + r) * (V * V);
+        }
+        const float mh = A.c1 * z1;
+        const float vh = A.c2 * z2;
+        if (MODE == kModeMoments) {
+          const int p = (int)(sx >> 16);
+          A.mhat[out_row * A.B + p] = mh;
+          A.vhat[out_row * A.B + p] = vh;
+        } else if (MODE == kModeSparse) {
+          st_param<BF>(A, s + (sx >> 16), th - A.lr * (mh / (sqrtf(vh) + A.eps)));
+        } else {
+          sm.slot[x] = f2u(A.lr * (mh / (sqrtf(vh) + A.eps)));
+        }
       }
     }
   }
@@ -1645,16 +1684,20 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
       }
     return;
   }
+  if (MODE == kModeSparse) {
+    if (A.touched && tid == 0) atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
+    return;
+  }
   __syncthreads();
 
-  // ---------------- parameters: theta = theta * decay - update on touched positions
+  // ---------------- dense mode: theta = theta * decay - update on touched positions
   if (!EARLY) issue_loads();
-  if (MODE != kModeMoments && vec_all) {
+  if (vec_all) {
     // no loads here: the stores need no waits
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      if (!((want >> it) & 1u)) continue;
       const int i0 = (it * kThreads + tid) * G;
+      if (i0 >= L) continue;
       const int w = i0 >> 5;
       const uint32_t word = sm.bits[w];
       const uint32_t gb = (word >> (i0 & 31)) & ((1u << G) - 1u);   // this group's touched bits
@@ -1666,7 +1709,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         th[e] = BF ? ((e & 1) ? u2f(vv[e >> 1] & 0xffff0000u) : u2f(vv[e >> 1] << 16)) : u2f(vv[e]);
 #pragma unroll
       for (int e = 0; e < G; ++e) {
-        if (MODE == kModeDense) th[e] = th[e] * A.decay;
+        th[e] = th[e] * A.decay;
         if ((gb >> e) & 1u) th[e] = th[e] - u2f(sm.slot[base + (uint32_t)__popc(gb & ((1u << e) - 1u))]);
       }
       if (BF) {
@@ -1681,21 +1724,20 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         __builtin_nontemporal_store(v0, reinterpret_cast<u32x4 *>(A.theta + s + i0));
       }
     }
-  } else if (MODE != kModeMoments) {
+  } else {
     // unaligned parameters or a partial group: element by element
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      if (!((want >> it) & 1u)) continue;
       const int i0 = (it * kThreads + tid) * G;
+      if (i0 >= L) continue;
       const int w = i0 >> 5;
       const uint32_t word = sm.bits[w];
       const uint32_t gb = (word >> (i0 & 31)) & ((1u << G) - 1u);
       const uint32_t base = sm.wbase[w] + (uint32_t)__popc(word & ((1u << (i0 & 31)) - 1u));
 #pragma unroll
       for (int e = 0; e < G; ++e) {
-        if (i0 + e < L && (MODE == kModeDense || ((gb >> e) & 1u))) {
-          float th = ld_param<BF>(A, s + i0 + e);
-          if (MODE == kModeDense) th = th * A.decay;
+        if (i0 + e < L) {
+          float th = ld_param<BF>(A, s + i0 + e) * A.decay;
           if ((gb >> e) & 1u) th = th - u2f(sm.slot[base + (uint32_t)__popc(gb & ((1u << e) - 1u))]);
           st_param<BF>(A, s + i0 + e, th);
         }
