@@ -410,6 +410,12 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
         }
       }
     }
+    // the fused bitmap's words alias the staged codes (word w is code word
+    // w mod 512 of chunk w / 512, which only thread w mod 512 reads, above):
+    // each thread clears its own words (ordered before the bitmap's use by the
+    // selection's barriers)
+    if (fb)
+      for (int w = tid; w < CPT * kChunkSpan / 32; w += kThreads) fb->bits[w] = 0u;
   } else {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -482,10 +488,6 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) tau = min(tau, sm.red[w]);
       const float tau_f = u2f(tau);
-      // the staged inputs are dead from here on: the bitmap's words are
-      // cleared (ordered before the selection by the barriers below)
-      if (fb)
-        for (int w = tid; w < CPT * kChunkSpan / 32; w += kThreads) fb->bits[w] = 0u;
       // (2) gather the candidates (key >= tau: !(|a| < tau), which NaN
       // passes) into LDS in index order
       uint32_t cnt[CPT], pos[CPT], C;
@@ -815,6 +817,10 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
   const float inv = (mx == mn) ? 0.f : 15.0f / (mx - mn);
   const bool flat = (mx == mn) || !(inv <= 3.402823466e38f);
   const uint32_t bkey = hashed ? 0u : philox_block_key(A.seed, A.t, j);
+  // the thread's LDS address, derived afresh: the one of the staged inputs'
+  // reads would otherwise be held across the selection (a spilled register)
+  int tq = (int)threadIdx.x;
+  asm volatile("" : "+v"(tq));
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     // keep the scheduler from interleaving chunks (register pressure)
@@ -827,7 +833,7 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
       uint32_t ev = 0, od = 0;
       uint32_t hw[kChunk / 2] = {0u, 0u, 0u, 0u};
       if (FULL && hashed) {
-        const u32x4 hv = reinterpret_cast<const u32x4 *>(lds_hash)[c * kThreads + tid];
+        const u32x4 hv = reinterpret_cast<const u32x4 *>(lds_hash)[c * kThreads + tq];
         hw[0] = hv.x; hw[1] = hv.y; hw[2] = hv.z; hw[3] = hv.w;
       }
 #pragma unroll
@@ -1874,7 +1880,9 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
   constexpr int W = CPT * kChunkSpan / 32;
   uint32_t *st_words = reinterpret_cast<uint32_t *>(&st);
   FusedBits fbits;
-  fbits.bits = st_words + CPT * kChunkSpan / 2;
+  // (the bitmap's words are the staged codes, from st.ef[0][0] on: the
+  // compressor clears each once its only reader has read it)
+  fbits.bits = &st.ef[0][0];
   fbits.ent = ent;
   fbits.es = es;
   fbits.M = A.m;
