@@ -1643,23 +1643,31 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         const uint32_t sx = sm.slot[x];
         const uint32_t c0 = MODE == kModeDense ? cst[u] : (x > 0 ? sm.slot[x - 1] & 0xffffu : 0u);
         const uint32_t c1 = MODE == kModeDense ? cen[u] : sx & 0xffffu;
-        for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
-          const uint32_t key = sm.col[a];
-          uint32_t b = a;
-          while (b > c0 && sm.col[b - 1] > key) {
-            sm.col[b] = sm.col[b - 1];
-            --b;
-          }
-          sm.col[b] = key;
-        }
         float z1 = 0.f, z2 = 0.f;
-        for (uint32_t a = c0; a < c1; ++a) {
-          const uint32_t key = sm.col[a];
+        auto add = [&](uint32_t key) {
           int r = A.tm - (int)(key >> 16);
           if (r < 0) r += M;
           const float V = bf16_bits_to_f32(key & 0xffffu);
           z1 = z1 + decay_factor(sm.beta, r) * V;
           z2 = z2 + decay_factor(sm.beta, M + r) * (V * V);
+        };
+        if (c1 - c0 <= 2u) {
+          // one or two keys (almost every column): ordered in registers
+          const uint32_t k0 = sm.col[c0];
+          const uint32_t k1 = (c1 - c0 == 2u) ? sm.col[c0 + 1] : k0;
+          add(min(k0, k1));
+          if (c1 - c0 == 2u) add(max(k0, k1));
+        } else {
+          for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
+            const uint32_t key = sm.col[a];
+            uint32_t b = a;
+            while (b > c0 && sm.col[b - 1] > key) {
+              sm.col[b] = sm.col[b - 1];
+              --b;
+            }
+            sm.col[b] = key;
+          }
+          for (uint32_t a = c0; a < c1; ++a) add(sm.col[a]);
         }
         const float mh = A.c1 * z1;
         const float vh = A.c2 * z2;
