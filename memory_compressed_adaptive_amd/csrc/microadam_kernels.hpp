@@ -624,9 +624,17 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
           // bitmap of the window's other rows
           const int t7 = tid - 64;
           if (EF && QMODE == kQBlock && lds_hash) {
+            // four consecutive words (one 16-byte LDS store) per thread and turn
             constexpr int kStride = kThreads - 64;
-            uint32_t st = pcg_state(philox_block_key(A.seed, A.t, j) + (uint32_t)t7);
-            for (int p = t7; p < L / 2; p += kStride, st += (uint32_t)kStride * kPcgMul) lds_hash[p] = pcg_out(st);
+            uint32_t st = pcg_state(philox_block_key(A.seed, A.t, j) + 4u * (uint32_t)t7);
+            for (int q = t7; q < L / 8; q += kStride, st += 4u * (uint32_t)kStride * kPcgMul) {
+              u32x4 v;
+              v.x = pcg_out(st);
+              v.y = pcg_out(st + kPcgMul);
+              v.z = pcg_out(st + 2u * kPcgMul);
+              v.w = pcg_out(st + 3u * kPcgMul);
+              reinterpret_cast<u32x4 *>(lds_hash)[q] = v;
+            }
           }
           if (fb) {
             for (int i = 0; i < fb->M; ++i) {
@@ -1036,6 +1044,24 @@ __device__ __forceinline__ void stage_beta(const ApplyArgs &A, float *beta, int 
     if (w0 + lane < n)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.betapow + w0 + lane),
                                        (lds_void_t *)(beta + w0), 4, 0, 0);
+}
+
+// The same factors by physical window row: beta[i] = beta1^r and
+// beta[m + i] = beta2^r, r = (tm - i) mod m the age of row i this step (the
+// column sums look them up by a key's row).
+__device__ __forceinline__ void stage_beta_rows(const ApplyArgs &A, float *beta, int tid) {
+  const int n = 2 * A.m;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int w0 = wv * 64; w0 < n; w0 += kThreads) {
+    const int i = w0 + lane;
+    if (i < n) {
+      const int half = i >= A.m ? A.m : 0;
+      int r = A.tm - (i - half);
+      if (r < 0) r += A.m;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(A.betapow + half + r),
+                                       (lds_void_t *)(beta + w0), 4, 0, 0);
+    }
+  }
 }
 
 // The update of block j.
@@ -1465,7 +1491,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   // ---------------- the block's m * k_b window entries into LDS (col), the
   // decay factors, a cleared bitmap
   for (int w = tid; w < W; w += kThreads) sm.bits[w] = 0u;
-  stage_beta(A, sm.beta, tid);
+  stage_beta_rows(A, sm.beta, tid);
   for (int x0 = wv * 64; x0 < E; x0 += kThreads) {
     const int x = x0 + lane;
     if (x < E) {
@@ -1644,12 +1670,11 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         const uint32_t c0 = MODE == kModeDense ? cst[u] : (x > 0 ? sm.slot[x - 1] & 0xffffu : 0u);
         const uint32_t c1 = MODE == kModeDense ? cen[u] : sx & 0xffffu;
         float z1 = 0.f, z2 = 0.f;
-        auto add = [&](uint32_t key) {
-          int r = A.tm - (int)(key >> 16);
-          if (r < 0) r += M;
+        auto add = [&](uint32_t key) {   // the factors of the key's row (staged by row)
+          const int row = (int)(key >> 16);
           const float V = bf16_bits_to_f32(key & 0xffffu);
-          z1 = z1 + decay_factor(sm.beta, r) * V;
-          z2 = z2 + decay_factor(sm.beta, M + r) * (V * V);
+          z1 = z1 + decay_factor(sm.beta, row) * V;
+          z2 = z2 + decay_factor(sm.beta, M + row) * (V * V);
         };
         if (c1 - c0 <= 2u) {
           // one or two keys (almost every column): ordered in registers
