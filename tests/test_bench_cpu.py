@@ -16,19 +16,31 @@ def _bench():
     return mod
 
 
-@pytest.mark.parametrize("workload,m,kernels", [
-    ("llama2_7b", 10, ["step_fused"]),
-    ("llama2_13b", 37, ["compress", "adamstats_apply"]),
-    ("llama2_13b", 20, ["compress", "adamstats_apply"]),
-])
-def test_committed_counter_summaries(workload, m, kernels):
-    # each summary names the kernels it measured, with positive byte counts; it
-    # is used exactly when it was taken on the kernel source as it is now
+def _summaries():
+    d = os.path.join(ROOT, "profiles")
+    return sorted(f for f in os.listdir(d) if f.startswith("hbm_traffic_") and f.endswith(".json"))
+
+
+def test_every_configuration_has_a_summary():
+    # the default line's headline and every entry of its configs array
+    want = {"hbm_traffic_llama2_7b_m10.json", "hbm_traffic_tiny_m10.json", "hbm_traffic_bert_base_m10.json",
+            "hbm_traffic_opt_1_3b_m10.json"} | {f"hbm_traffic_llama2_13b_m{m}.json" for m in (1, 10, 20, 37)}
+    assert want <= set(_summaries())
+
+
+@pytest.mark.parametrize("name", _summaries())
+def test_committed_counter_summaries(name):
+    # each summary names the kernels it measured, with positive byte counts (the
+    # fused step at least; a partial last block adds the two general kernels);
+    # it is used exactly when it was taken on the kernel source as it is now
     b = _bench()
-    rec = json.load(open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_m{m}.json")))
-    assert rec["workload"] == workload and rec["m"] == m and set(rec["kernels"]) == set(kernels)
-    for k in rec["kernels"].values():
-        assert k["fetch_bytes"] > 0 and k["write_bytes"] > 0 and k["launches_per_step"] >= 1
+    rec = json.load(open(os.path.join(ROOT, "profiles", name)))
+    workload, m, kernels = rec["workload"], rec["m"], sorted(rec["kernels"])
+    assert name == f"hbm_traffic_{workload}_m{m}.json"
+    assert "step_fused" in kernels and set(kernels) <= {"step_fused", "compress", "adamstats_apply"}
+    k = rec["kernels"]["step_fused"]
+    assert k["fetch_bytes"] > 0 and k["write_bytes"] > 0 and k["launches_per_step"] >= 1
+    assert rec["fetch_scale"] > 0 and rec["write_scale"] > 0
     t = b.load_traffic(workload, m, False, kernels)
     assert (t is not None) == (rec["kernel_source_sha256"] == b.kernel_source_sha())
 
@@ -41,7 +53,7 @@ def test_counters_apply_only_to_the_default_step_and_its_kernels():
     assert b.load_traffic("llama2_7b", 10, False, ["compress", "adamstats_apply"]) is None
     assert b.load_traffic("llama2_7b", 10, False, ["step_fused", "compress"]) is None
     # nor a configuration without a summary
-    assert b.load_traffic("bert_base", 10, False, ["step_fused"]) is None
+    assert b.load_traffic("llama2_13b", 30, False, ["step_fused"]) is None
 
 
 @pytest.mark.parametrize("which", [0, 1])
