@@ -1046,6 +1046,24 @@ __device__ __forceinline__ void stage_beta(const ApplyArgs &A, float *beta, int 
                                        (lds_void_t *)(beta + w0), 4, 0, 0);
 }
 
+// sqrtf(x), correctly rounded, for every active lane.  Where every active
+// lane's x is finite and at least 2^-96: the hardware estimate (within one
+// ulp) replaced by a neighbour when the residual x - n * s of that neighbour
+// n says it is nearer (the correction sqrtf itself applies; its scaling of
+// small inputs and its special cases are not needed in that range).  For any
+// other wave, sqrtf.  Correct rounding makes the two agree bit for bit.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  // x in [2^-96, FLT_MAX] (not negative, not NaN): one unsigned compare
+  const bool wide = f2u(x) - 0x0f800000u <= 0x7f7fffffu - 0x0f800000u;
+  if (__builtin_amdgcn_ballot_w64(wide) == __builtin_amdgcn_read_exec()) {
+    const float s = __builtin_amdgcn_sqrtf(x);
+    const float lo = u2f(f2u(s) - 1u), hi = u2f(f2u(s) + 1u);
+    const float r = (fmaf(-lo, s, x) <= 0.0f) ? lo : s;
+    return (fmaf(-hi, s, x) > 0.0f) ? hi : r;
+  }
+  return sqrtf(x);
+}
+
 // The same factors by physical window row: beta[i] = beta1^r and
 // beta[m + i] = beta2^r, r = (tm - i) mod m the age of row i this step (the
 // column sums look them up by a key's row).
@@ -1332,7 +1350,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
         if (x < n) {
           const float mh = A.c1 * s_z1[x];
           const float vh = A.c2 * s_z2[x];
-          st_param<BF>(A, s + s_pos[x], th - A.lr * (mh / (sqrtf(vh) + A.eps)));
+          st_param<BF>(A, s + s_pos[x], th - A.lr * (mh / (sqrt_rn(vh) + A.eps)));
         }
       }
     } else if (MODE == kModeDense) {
@@ -1351,7 +1369,7 @@ __device__ __forceinline__ void apply_block(const ApplyArgs &A, int64_t j, int64
               if (sl < n) {
                 const float mh = A.c1 * s_z1[sl];
                 const float vh = A.c2 * s_z2[sl];
-                th[c][e] = th[c][e] - A.lr * (mh / (sqrtf(vh) + A.eps));
+                th[c][e] = th[c][e] - A.lr * (mh / (sqrt_rn(vh) + A.eps));
               }
             }
           }
@@ -1701,9 +1719,9 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
           A.mhat[out_row * A.B + p] = mh;
           A.vhat[out_row * A.B + p] = vh;
         } else if (MODE == kModeSparse) {
-          st_param<BF>(A, s + (sx >> 16), th - A.lr * (mh / (sqrtf(vh) + A.eps)));
+          st_param<BF>(A, s + (sx >> 16), th - A.lr * (mh / (sqrt_rn(vh) + A.eps)));
         } else {
-          sm.slot[x] = f2u(A.lr * (mh / (sqrtf(vh) + A.eps)));
+          sm.slot[x] = f2u(A.lr * (mh / (sqrt_rn(vh) + A.eps)));
         }
       }
     }

@@ -539,6 +539,35 @@ def test_nonfinite_gradients(B, flags, gq, wd):
                 grad_fn=_nonfinite_grads(B), global_quant=gq)
 
 
+def _tiny_grads(kind):
+    # "mixed": a background of 1e-30 with 2 % of the entries at magnitudes
+    # log-uniform in 1e-17 .. 1e-12, so the selected values' v_hat fall on
+    # both sides of 2^-96 (the square root's two paths, often in one wave);
+    # "subnormal": everything in 1e-38 .. 1e-20 (V^2 subnormal or zero)
+    def fn(rng, d, t):
+        if kind == "mixed":
+            mag = np.full(d, 1e-30)
+            big = rng.random(d) < 0.02
+            mag[big] = 10.0 ** rng.uniform(-17, -12, int(big.sum()))
+        else:
+            mag = 10.0 ** rng.uniform(-38, -20, d)
+        return O.bf16_rne((rng.standard_normal(d) * mag).astype(np.float32))
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["mixed", "subnormal"])
+@pytest.mark.parametrize("m,row_sums,wd", [(4, False, 0.0), (4, True, 0.0), (4, False, 0.1), (20, False, 0.0),
+                                           (20, False, 0.1)])
+def test_tiny_gradients_square_root_paths(kind, m, row_sums, wd):
+    # the update's correctly rounded square root: its fast path where a wave's
+    # v_hat are all in [2^-96, FLT_MAX], sqrtf otherwise; both equal the
+    # oracle's bit for bit, as do the subnormal sums (row sums and column
+    # sums, sparse and dense)
+    d, B = 5 * 16384 + 321, 16384
+    full_parity(f"tiny grads {kind} m={m} rows={row_sums} wd={wd}", d, B, d // 100, m, m + 2,
+                wd=wd, grad_fn=_tiny_grads(kind), gpu_only_flags=L.MA_FLAG_ROW_SUMS if row_sums else 0)
+
+
 # ---------------------------------------------------------------- the two update algorithms
 
 @pytest.mark.parametrize("d,B,k,m,wd,flags", [
