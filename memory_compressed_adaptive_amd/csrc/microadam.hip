@@ -491,9 +491,9 @@ hipError_t dispatch_global_p2(int cpt, bool aligned, const CompressArgs &a, int6
 // the compressor's staging) where its LDS holds the window, and
 // step_csu_kernel where only the column-sorted update fits (longer windows).
 // Measured at LLaMA-2 shapes: step_full_kernel is faster at m <= 10 (13B:
-// 16.7 vs 21.5 ms at m = 1, 25.4 vs 29.2 ms at m = 10), step_csu_kernel at
-// m = 20 and 37 (33.3 and 38.8 ms against 33.7 and 69.9 ms as two kernels
-// with row sums).
+// 16.9 vs 17.9 ms at m = 1, 27.6 vs 29.5 ms at m = 10; 7B, m = 10: 15.0 vs
+// 15.5 ms), step_csu_kernel at m = 20 and 37 (when it came: 33.3 and 38.8 ms
+// against 33.7 and 69.9 ms as two kernels with row sums).
 UpdLaunch upd_launch(const ma_ctx *h) {
   const bool csu = h->csu_ok && !(h->flags & MA_FLAG_ROW_SUMS);
   const bool fcsu = csu && h->fused_csu_ok && !h->fused_ok;

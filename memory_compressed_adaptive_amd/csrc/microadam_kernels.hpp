@@ -1694,12 +1694,19 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
           z1 = z1 + decay_factor(sm.beta, row) * V;
           z2 = z2 + decay_factor(sm.beta, M + row) * (V * V);
         };
-        if (c1 - c0 <= 2u) {
-          // one or two keys (almost every column): ordered in registers
+        if (c1 - c0 <= 3u) {
+          // one to three keys (almost every column): a three-key sorting
+          // network in registers; absent keys are all ones, above every key
+          // (rows < 65535) and never added
+          const uint32_t n = c1 - c0;
           const uint32_t k0 = sm.col[c0];
-          const uint32_t k1 = (c1 - c0 == 2u) ? sm.col[c0 + 1] : k0;
-          add(min(k0, k1));
-          if (c1 - c0 == 2u) add(max(k0, k1));
+          const uint32_t k1 = n >= 2u ? sm.col[c0 + 1] : 0xffffffffu;
+          const uint32_t k2 = n >= 3u ? sm.col[c0 + 2] : 0xffffffffu;
+          const uint32_t a = min(k0, k1), b = max(k0, k1);
+          const uint32_t t = max(a, k2);
+          add(min(a, k2));
+          if (n >= 2u) add(min(b, t));
+          if (n >= 3u) add(max(b, t));
         } else {
           for (uint32_t a = c0 + 1; a < c1; ++a) {   // insertion sort of a few keys
             const uint32_t key = sm.col[a];
