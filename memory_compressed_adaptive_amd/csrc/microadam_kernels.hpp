@@ -11,21 +11,27 @@
 //               chunk); g and the 4-bit codes are read once and the codes
 //               written once.
 //   apply     = adamstats_apply.  The m window segments of the block are
-//               turned into a bitmap of touched positions, each touched
-//               position gets a compact LDS slot, the rows are summed into the
-//               slots in row order, and only the touched parameters are read
-//               and written.
+//               turned into a bitmap of touched positions and each touched
+//               position gets a compact LDS slot.  Then either the rows are
+//               summed into the slots one row at a time (apply_block, short
+//               windows), or the entries are sorted by slot (a counting sort
+//               in LDS) and each slot's column is summed by one thread
+//               (apply_block_csu, long windows).  Only the touched parameters
+//               are read and written (sparse mode), or all of them with
+//               decoupled decay (dense mode).
 //
-// step_full_kernel runs both phases of a block in one workgroup (the default
-// for full, aligned blocks whose window fits its LDS); compress_full_kernel /
-// compress_kernel and apply_kernel run them as two kernels (a partial last
-// block, long windows, unaligned inputs).
+// step_full_kernel (row sums) and step_csu_kernel (column sums) run both
+// phases of a block in one workgroup: the default for full, aligned blocks,
+// the first where its LDS holds the window, the second for longer windows.
+// compress_full_kernel / compress_kernel and apply_kernel / apply_csu_kernel
+// run them as two kernels (a partial last block, windows too long for either
+// fused kernel, unaligned inputs).
 //
 // Bit-exactness with the CPU oracle rests on: fp32 with one rounding per
 // operation (built with -ffp-contract=off), the explicit fmaf of the
 // dequantizer, correctly rounded division and square root, the same host
-// constants, and a fixed accumulation order (rows in physical order; indices
-// within a row are unique).
+// constants, and a fixed accumulation order (each position's entries added
+// in physical row order, by either algorithm).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -1485,9 +1491,11 @@ __device__ __forceinline__ int csu_row(int x, float inv_kb) {
 // the block's window offset and quota, already known (re-reading them from
 // global memory would wait for all the vector memory in flight, the
 // compressor's stores included).
-// EARLY: the parameters' loads are issued before the column sums (their
-// latency overlaps them; 4 words per load held meanwhile), else after them
-// (the fused kernel, whose registers are taken by the compressor's budget).
+// EARLY (dense mode): the block's 16-byte parameter groups are loaded before
+// the column sums (their latency overlaps them; 4 words per load held
+// meanwhile), else after them (the fused kernel, whose registers are taken by
+// the compressor's budget).  The sparse mode loads each touched parameter
+// before the sums in either case, one word per slot.
 template <int CPT, int MODE, bool ALIGNED, bool BF = false, bool EARLY = true>
 __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, int64_t out_row, const CsuSmem &sm,
                                                 const uint32_t *newrow = nullptr, int64_t pre_off = 0,
