@@ -485,18 +485,24 @@ hipError_t dispatch_global_p2(int cpt, bool aligned, const CompressArgs &a, int6
 }
 
 
-// The update kernels a handle uses: column-sorted where the block's window
-// fits them, unless MA_FLAG_ROW_SUMS asks for the row-by-row sums.
-// Full blocks run step_full_kernel (row-by-row sums, window preloaded during
-// the compressor's staging) where its LDS holds the window, and
-// step_csu_kernel where only the column-sorted update fits (longer windows).
-// Measured at LLaMA-2 shapes: step_full_kernel is faster at m <= 10 (13B:
-// 16.9 vs 17.9 ms at m = 1, 27.6 vs 29.5 ms at m = 10; 7B, m = 10: 15.0 vs
-// 15.5 ms), step_csu_kernel at m = 20 and 37 (when it came: 33.3 and 38.8 ms
-// against 33.7 and 69.9 ms as two kernels with row sums).
-UpdLaunch upd_launch(const ma_ctx *h) {
+// The update kernels a step uses: column-sorted where the block's window fits
+// them, unless MA_FLAG_ROW_SUMS asks for the row-by-row sums.  Full blocks
+// run step_csu_kernel (column sums) where step_full_kernel's LDS cannot hold
+// the window, for the dense update (decay), and for fp32 parameters from
+// kCsuFusedMinWindow rows up; step_full_kernel (row-by-row sums, window
+// preloaded during the compressor's staging) otherwise.  Measured (ms per
+// step, column sums vs row sums, one process): m = 10: 7B 15.13 vs 15.50 and
+// 13.18 vs 13.10 on two boxes, BERT-Base 0.291 vs 0.304, OPT-1.3B 2.96 vs
+// 3.04, 13B 25.40 vs 25.25; 7B with decay 0.01 15.10 vs 17.50 (bf16 13.59 vs
+// 16.40); 7B bf16 without decay 11.45 vs 11.13; 13B m = 4 20.4 vs 19.6, m = 1
+// 16.75 vs 15.80; at m = 20 and 37 step_csu_kernel against the two kernels
+// with row sums, when it came: 33.3 and 38.8 vs 33.7 and 69.9.
+constexpr int kCsuFusedMinWindow = 10;
+
+UpdLaunch upd_launch(const ma_ctx *h, bool dense = false, bool bf = false) {
   const bool csu = h->csu_ok && !(h->flags & MA_FLAG_ROW_SUMS);
-  const bool fcsu = csu && h->fused_csu_ok && !h->fused_ok;
+  const bool prefer = dense || (!bf && h->m >= kCsuFusedMinWindow);
+  const bool fcsu = csu && h->fused_csu_ok && (!h->fused_ok || prefer);
   return UpdLaunch{csu, csu ? h->csu_lds : h->apply_lds, fcsu, h->fused_csu_lds};
 }
 
@@ -742,7 +748,6 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   const float c1 = (float)((1.0 - b1) / (1.0 - std::pow(b1, (double)t)));
   const float c2 = (float)((1.0 - b2) / (1.0 - std::pow(b2, (double)t)));
   const float decay = (float)(1.0 - (double)h->lr * (double)h->wd);
-  const UpdLaunch ul = upd_launch(h);
 
   CompressArgs ca{};
   ca.g = grads;
@@ -775,6 +780,7 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   if (h->flags & MA_FLAG_FORCE_DENSE) mode = kModeDense;
   if (h->flags & MA_FLAG_FORCE_SPARSE) mode = kModeSparse;
   if (decay != 1.0f) mode = kModeDense;
+  const UpdLaunch ul = upd_launch(h, mode == kModeDense, bf);
 
   // The blocks are cut into h->chunks ranges.  Compress of range i runs on
   // the caller's stream; the update of range i runs on the library's side
