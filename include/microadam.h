@@ -66,8 +66,10 @@ enum {
 #define MA_FLAG_UNFUSED 16u     /* run compress and update as two kernels even where the
                                    fused per-block kernel applies (same results) */
 #define MA_FLAG_ROW_SUMS 64u     /* AdamStats by adding the window rows one at a time into
-                                   per-slot sums (a barrier per row) instead of the default
-                                   column-sorted update (same results) */
+                                   per-slot sums (a barrier per row) wherever the library would
+                                   otherwise sort the window by position and sum each column
+                                   (its choice per step: longer windows, decay, fp32 parameters
+                                   from 10 rows; same results either way) */
 #define MA_FLAG_GLOBAL_QUANT 32u /* one (delta, Delta) pair over all d, the literal scalar form
                                    of the first paragraph (default: one pair per B_d block).
                                    Costs a second pass over gradients and codes.  The pair is
