@@ -519,8 +519,12 @@ __device__ __forceinline__ bool compress_block(const CompressArgs &A, CompressSm
           for (int e = 0; e < kChunk; ++e) {
             const int i = c * kChunkSpan + tid * kChunk + e;
             const bool cd = MA_VALID(i) && !(fabsf(a[c][e]) < tau_g);
-            if (cd) sm.cand[p] = make_uint2(f2u(a[c][e]), (uint32_t)i);
-            p += cd ? 1u : 0u;
+            // (a wave with no candidate at this element skips it: a third
+            // of the waves at k = d/100)
+            if (__builtin_amdgcn_ballot_w64(cd)) {
+              if (cd) sm.cand[p] = make_uint2(f2u(a[c][e]), (uint32_t)i);
+              p += cd ? 1u : 0u;
+            }
           }
         }
         __syncthreads();
