@@ -21,8 +21,9 @@
 //               decoupled decay (dense mode).
 //
 // step_full_kernel (row sums) and step_csu_kernel (column sums) run both
-// phases of a block in one workgroup: the default for full, aligned blocks,
-// the first where its LDS holds the window, the second for longer windows.
+// phases of a block in one workgroup: the default for full, aligned blocks.
+// The host picks one per step by window length, update mode and parameter
+// type (step_full_kernel only where its LDS holds the window).
 // compress_full_kernel / compress_kernel and apply_kernel / apply_csu_kernel
 // run them as two kernels (a partial last block, windows too long for either
 // fused kernel, unaligned inputs).
