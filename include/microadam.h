@@ -60,9 +60,16 @@ enum {
 
 /* Flags for ma_set_flags. */
 #define MA_FLAG_NO_EF 1u        /* a_t = g_t: stored error neither read nor rewritten */
-#define MA_FLAG_FORCE_DENSE 4u  /* stream the parameters in the update (same results) */
+#define MA_FLAG_FORCE_DENSE 4u  /* stream the parameters through registers in the update
+                                   (same results) */
 #define MA_FLAG_FORCE_SPARSE 8u /* gather only touched parameters (same results; ignored
                                    when weight decay makes every parameter change) */
+/* Without either flag, full blocks of 16-byte aligned fp32 parameters whose
+ * window leaves room in the fused kernel's LDS (m * k_b up to about 2,000
+ * entries at B_d = 16384) pass through LDS in one or two chunks: the touched
+ * positions are updated there and every parameter line is written back whole.
+ * Elsewhere the touched parameters are gathered (no decay) or all of them
+ * streamed (decay).  Every form gives the same bits. */
 #define MA_FLAG_UNFUSED 16u     /* run compress and update as two kernels even where the
                                    fused per-block kernel applies (same results) */
 #define MA_FLAG_ROW_SUMS 64u     /* AdamStats by adding the window rows one at a time into

@@ -107,6 +107,7 @@ struct ma_ctx {
   bool fused_csu_ok = false;   // full blocks fit step_csu_kernel (three workgroups per CU)
   size_t fused_csu_lds = 0;
   int32_t fused_union_words = 0;
+  int32_t thl_off = 0, thl_n = 0;   // step_csu_kernel: LDS chunk of the parameters (0: none)
 
   uint8_t *codes = nullptr;
   size_t codes_bytes = 0, codes_alloc = 0;
@@ -278,6 +279,7 @@ struct UpdLaunch {
   size_t lds;
   bool fused_csu;      // full blocks: step_csu_kernel instead of step_full_kernel
   size_t fused_lds;    // its dynamic LDS
+  bool thl;            // step_csu_kernel with fp32 parameters through LDS (16-byte aligned ones)
 };
 
 template <int CPT, int MODE, bool AL, bool BF>
@@ -316,7 +318,16 @@ hipError_t dispatch_apply(int cpt, int mode, bool aligned, const ApplyArgs &a, i
 // the global quantizer's first pass in place of the compressor.
 template <int CPT, bool EF, bool BF, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
 hipError_t launch_fused(const CompressArgs &c, const ApplyArgs &a, int64_t n_full, const UpdLaunch &apply_lds, hipStream_t s) {
-  if (apply_lds.fused_csu) {
+  bool launched = false;
+  if constexpr (!BF && PAL && QMODE == kQBlock) {
+    if (apply_lds.fused_csu && apply_lds.thl) {
+      hipLaunchKernelGGL((step_csu_kernel<CPT, EF, BF, QMODE, MODE, PAL, true>), dim3((unsigned)n_full),
+                         dim3(kThreads), 0, s, c, a, (int64_t)0);
+      launched = true;
+    }
+  }
+  if (launched) {
+  } else if (apply_lds.fused_csu) {
     hipLaunchKernelGGL((step_csu_kernel<CPT, EF, BF, QMODE, MODE, PAL>), dim3((unsigned)n_full), dim3(kThreads), 0,
                        s, c, a, (int64_t)0);
   } else {
@@ -503,7 +514,8 @@ UpdLaunch upd_launch(const ma_ctx *h, bool dense = false, bool bf = false) {
   const bool csu = h->csu_ok && !(h->flags & MA_FLAG_ROW_SUMS);
   const bool prefer = dense || (!bf && h->m >= kCsuFusedMinWindow);
   const bool fcsu = csu && h->fused_csu_ok && (!h->fused_ok || prefer);
-  return UpdLaunch{csu, csu ? h->csu_lds : h->apply_lds, fcsu, h->fused_csu_lds};
+  const bool thl = fcsu && !bf && h->thl_n > 0 && !(h->flags & (MA_FLAG_FORCE_SPARSE | MA_FLAG_FORCE_DENSE));
+  return UpdLaunch{csu, csu ? h->csu_lds : h->apply_lds, fcsu, h->fused_csu_lds, thl};
 }
 
 ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float decay) {
@@ -521,6 +533,8 @@ ApplyArgs make_apply_args(const ma_ctx *h, int64_t t, float c1, float c2, float 
   a.ent_cap = h->ent_cap;
   a.csu_slots = h->csu_slots;
   a.fused_union_words = h->fused_union_words;
+  a.thl_off = h->thl_off;
+  a.thl_n = h->thl_n;
   a.c1 = c1;
   a.c2 = c2;
   a.lr = h->lr;
@@ -623,6 +637,19 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     h->fused_union_words = (int32_t)union_words;
     h->fused_csu_lds = 4 * (union_words + (size_t)kb_max);
     h->fused_csu_ok = h->csu_ok && h->cpt <= 4 && B_d == h->cpt * kChunkSpan && h->fused_csu_lds <= kFusedCsuLdsLimit;
+    // fp32 parameters through LDS in the fused kernel: the whole block or
+    // half of it (more chunks expose the loads of each, measured slower:
+    // LLaMA-2-13B m = 20, four chunks, 32.6 against 30.2 ms), behind the
+    // update's arrays (bitmap, slot bases, decay factors, slots, entries),
+    // 16-byte aligned, within the static buffer
+    const size_t thl_off = (2 * (size_t)W + 2 * (size_t)m + (size_t)csu_slots + (size_t)ents + 3) & ~(size_t)3;
+    if (h->fused_csu_ok)
+      for (int64_t n = B_d; n >= B_d / 2 && n >= 4 * kThreads; n /= 2)
+        if (thl_off + (size_t)n <= (size_t)kFusedCsuWords) {
+          h->thl_off = (int32_t)thl_off;
+          h->thl_n = (int32_t)n;
+          break;
+        }
   }
   h->chunks = h->n_b >= 8192 ? 8 : 1;
 

@@ -997,6 +997,7 @@ struct ApplyArgs {
   int32_t ent_cap;          // window entries the LDS copy holds (m*k_b must fit to use it)
   int32_t csu_slots;        // column-sorted update: slot words (min(B_d, m * max k_b))
   int32_t fused_union_words;  // step_csu_kernel: LDS words shared by its two phases
+  int32_t thl_off, thl_n;   // step_csu_kernel, THL: LDS word offset and length (floats) of the parameter chunk
   float c1, c2, lr, eps, decay;
 };
 
@@ -1489,6 +1490,17 @@ __device__ __forceinline__ int csu_row(int x, float inv_kb) {
   return (int)(((float)x + 0.5f) * inv_kb);
 }
 
+// Issues the LDS-DMA of n fp32 parameters from element i0 (16-byte aligned;
+// n a multiple of 4 * kThreads) into R, 16 bytes per lane.  The caller waits
+// for its vector memory and a barrier before R is read.
+__device__ __forceinline__ void stage_theta_chunk(const ApplyArgs &A, float *R, int64_t i0, int n, int tid) {
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(A.theta + i0);
+  u32x4 *dst = reinterpret_cast<u32x4 *>(R);
+  for (int q = tid; q < n / 4; q += kThreads)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + q), (lds_void_t *)(dst + (q & ~63)), 16, 0,
+                                     0);
+}
+
 // MODE as apply_block (kModeSparse, kModeDense, kModeMoments).
 // newrow (optional): window row t mod m of the block, already in LDS (the
 // fused kernel's compressor wrote it there beside its global copy); that row
@@ -1498,13 +1510,21 @@ __device__ __forceinline__ int csu_row(int x, float inv_kb) {
 // compressor's stores included).
 // EARLY (dense mode): the block's 16-byte parameter groups are loaded before
 // the column sums (their latency overlaps them; 4 words per load held
-// meanwhile), else after them (the fused kernel, whose registers are taken by
-// the compressor's budget).  The sparse mode loads each touched parameter
+// meanwhile), else after them.  The sparse mode loads each touched parameter
 // before the sums in either case, one word per slot.
-template <int CPT, int MODE, bool ALIGNED, bool BF = false, bool EARLY = true>
+// THL (fp32 parameters, 16-byte aligned, full block; sparse or dense mode):
+// the parameters pass through LDS in chunks of thl_n floats at thl, every
+// 128-byte line read and written whole: each chunk comes in by LDS-DMA (the
+// first one in flight during the sort), the slot threads update their touched
+// positions in LDS (theta * decay - update), and the chunk goes back in
+// coalesced 16-byte stores, the untouched positions scaled by the decay.
+// Whole-line write-back costs less HBM time than the dirty 32-byte sectors of
+// a scattered one, even though it moves every byte.
+template <int CPT, int MODE, bool ALIGNED, bool BF = false, bool EARLY = true, bool THL = false>
 __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, int64_t out_row, const CsuSmem &sm,
                                                 const uint32_t *newrow = nullptr, int64_t pre_off = 0,
-                                                int pre_kb = -1) {
+                                                int pre_kb = -1, float *thl = nullptr) {
+  static_assert(!THL || (!BF && ALIGNED && MODE != kModeMoments), "THL: fp32, aligned parameters, an update mode");
   constexpr int W = CPT * kChunkSpan / 32;           // bitmap words
   constexpr int WPT = (W + kThreads - 1) / kThreads; // words a thread owns
   int tid = (int)threadIdx.x;
@@ -1536,6 +1556,8 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
     for (int q = tid; q < kb; q += kThreads) sm.col[A.tm * kb + q] = newrow[q];
   wait_vm_all();
   __syncthreads();
+  // THL: the first parameter chunk, in flight while the window is sorted
+  if (THL) stage_theta_chunk(A, thl, s, A.thl_n, tid);
 
   // ---------------- each thread's entries (x = tid + u * 512) into registers,
   // and the bitmap of the touched positions.  A zero value adds nothing
@@ -1642,7 +1664,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   const bool vec_all = ALIGNED && (L % G) == 0;
   u32x4 raw[MODE == kModeDense ? NIT : 1];
   auto issue_loads = [&]() {
-    if (MODE == kModeDense) {
+    if (MODE == kModeDense && !THL) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int i0 = (it * kThreads + tid) * G;
@@ -1664,9 +1686,13 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   // replaces the slot word, so each slot's column start and end are read
   // first, before a barrier.
   const int nU = (int)((U + kThreads - 1) / kThreads);   // slots per thread, uniform
-  uint32_t cst[MODE == kModeDense ? kCsuPerThread : 1], cen[MODE == kModeDense ? kCsuPerThread : 1];
-  float thv[MODE == kModeSparse ? kCsuPerThread : 1];
-  if (MODE == kModeDense) {
+  constexpr bool kDenseSlots = MODE == kModeDense && !THL;   // update values replace the slot words
+  constexpr bool kGather = MODE == kModeSparse && !THL;      // touched parameters gathered by slot
+  uint32_t cst[kDenseSlots ? kCsuPerThread : 1], cen[kDenseSlots ? kCsuPerThread : 1];
+  float thv[kGather ? kCsuPerThread : 1];
+  float thu[THL ? kCsuPerThread : 1];        // THL: each slot's update value and position
+  uint32_t thp[THL ? kCsuPerThread : 1];
+  if (kDenseSlots) {
 #pragma unroll
     for (int u = 0; u < kCsuPerThread; ++u) {
       cst[u] = cen[u] = 0u;
@@ -1677,7 +1703,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
       }
     }
     __syncthreads();
-  } else if (MODE == kModeSparse) {
+  } else if (kGather) {
     if (U == 0) return;
     // (all of them, unconditionally: a scalar branch between a load and its
     // use makes the compiler wait for all vector memory there)
@@ -1690,16 +1716,20 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
 #pragma unroll
   for (int u = 0; u < kCsuPerThread; ++u) {
     const uint32_t x = (uint32_t)tid + (uint32_t)(u * kThreads);
-    if (MODE == kModeSparse || u < nU) {
+    if (THL) {
+      thu[u] = 0.f;
+      thp[u] = 0xffffffffu;
+    }
+    if (kGather || u < nU) {
       float th = 0.f;
-      if (MODE == kModeSparse) {
+      if (kGather) {
         th = thv[u];
         asm volatile("" ::"v"(th));   // the wait for the load, on every path
       }
       if (x < U) {
         const uint32_t sx = sm.slot[x];
-        const uint32_t c0 = MODE == kModeDense ? cst[u] : (x > 0 ? sm.slot[x - 1] & 0xffffu : 0u);
-        const uint32_t c1 = MODE == kModeDense ? cen[u] : sx & 0xffffu;
+        const uint32_t c0 = kDenseSlots ? cst[u] : (x > 0 ? sm.slot[x - 1] & 0xffffu : 0u);
+        const uint32_t c1 = kDenseSlots ? cen[u] : sx & 0xffffu;
         float z1 = 0.f, z2 = 0.f;
         auto add = [&](uint32_t key) {   // the factors of the key's row (staged by row)
           const int row = (int)(key >> 16);
@@ -1734,7 +1764,10 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         }
         const float mh = A.c1 * z1;
         const float vh = A.c2 * z2;
-        if (MODE == kModeMoments) {
+        if (THL) {
+          thu[u] = A.lr * (mh / (sqrt_rn(vh) + A.eps));
+          thp[u] = sx >> 16;
+        } else if (MODE == kModeMoments) {
           const int p = (int)(sx >> 16);
           A.mhat[out_row * A.B + p] = mh;
           A.vhat[out_row * A.B + p] = vh;
@@ -1745,6 +1778,44 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         }
       }
     }
+  }
+  if (THL) {
+    // ---------------- the parameters through LDS, chunk by chunk
+    const bool decays = A.decay != 1.0f;
+    const int cn = A.thl_n;
+    const u32x4 *R4 = reinterpret_cast<const u32x4 *>(thl);
+    for (int c0 = 0; c0 < L; c0 += cn) {
+      if (c0 > 0) stage_theta_chunk(A, thl, s + c0, cn, tid);
+      wait_vm_all();
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kCsuPerThread; ++u) {
+        if (u < nU) {
+          const uint32_t q = thp[u] - (uint32_t)c0;
+          if (q < (uint32_t)cn) {
+            float th = thl[q];
+            if (decays) th = th * A.decay;
+            thl[q] = th - thu[u];
+          }
+        }
+      }
+      __syncthreads();
+      for (int q = tid; q < cn / 4; q += kThreads) {
+        u32x4 v = R4[q];
+        if (decays) {
+          const int i0 = c0 + 4 * q;
+          const uint32_t gb = (sm.bits[i0 >> 5] >> (i0 & 31)) & 15u;   // touched ones are already done
+          if (!(gb & 1u)) v.x = f2u(u2f(v.x) * A.decay);
+          if (!(gb & 2u)) v.y = f2u(u2f(v.y) * A.decay);
+          if (!(gb & 4u)) v.z = f2u(u2f(v.z) * A.decay);
+          if (!(gb & 8u)) v.w = f2u(u2f(v.w) * A.decay);
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(A.theta + s + c0) + q);
+      }
+      if (c0 + cn < L) __syncthreads();   // the next chunk's loads overwrite the LDS chunk
+    }
+    if (A.touched && tid == 0) atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
+    return;
   }
   if (MODE == kModeMoments) {
     // positions without an entry: 0
@@ -1769,6 +1840,9 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
 
   // ---------------- dense mode: theta = theta * decay - update on touched positions
   if (!EARLY) issue_loads();
+  // (without decay, the factor 1 is not applied: the stored value is the
+  // loaded one, as in the sparse mode)
+  const bool decays = A.decay != 1.0f;
   if (vec_all) {
     // no loads here: the stores need no waits
 #pragma unroll
@@ -1786,7 +1860,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
         th[e] = BF ? ((e & 1) ? u2f(vv[e >> 1] & 0xffff0000u) : u2f(vv[e >> 1] << 16)) : u2f(vv[e]);
 #pragma unroll
       for (int e = 0; e < G; ++e) {
-        th[e] = th[e] * A.decay;
+        if (decays) th[e] = th[e] * A.decay;
         if ((gb >> e) & 1u) th[e] = th[e] - u2f(sm.slot[base + (uint32_t)__popc(gb & ((1u << e) - 1u))]);
       }
       if (BF) {
@@ -1997,7 +2071,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
 // granules), the scan words included.
 constexpr int kFusedCsuWords = (53760 - 64) / 4;
 
-template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false>
+template <int CPT, bool EF, bool BF = false, int QMODE = kQBlock, int MODE = kModeSparse, bool PAL = false,
+          bool THL = false>
 __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_csu_kernel(CompressArgs C, ApplyArgs A,
                                                                             int64_t first_block) {
   static_assert(QMODE == kQBlock || (QMODE == kQGlobal1 && EF), "the fused kernel runs a step or a first pass");
@@ -2017,7 +2092,8 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_csu_kernel(Compr
                                                                    reinterpret_cast<uint32_t *>(st), nullptr);
   if (!done) return;
   __syncthreads();
-  apply_block_csu<CPT, MODE, PAL, BF, false>(A, j, 0, csu_smem<CPT>(A, lds, s_cnt), newrow, in.off, in.kb);
+  apply_block_csu<CPT, MODE, PAL, BF, MODE == kModeDense, THL>(A, j, 0, csu_smem<CPT>(A, lds, s_cnt), newrow, in.off,
+                                                                in.kb, reinterpret_cast<float *>(lds + A.thl_off));
 }
 
 }  // namespace microadam

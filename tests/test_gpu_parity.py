@@ -140,6 +140,28 @@ def test_fused_step_with_decay(B):
     full_parity(f"fused decay B={B}", d, B, d // 100, 10, 12, lr=1e-2, wd=0.1)
 
 
+@pytest.mark.parametrize("B,wd,flags", [
+    (16384, 0.0, 0),                          # parameters through LDS in two chunks
+    (16384, 0.0, L.MA_FLAG_FORCE_SPARSE),     # the touched parameters gathered by slot instead
+    (16384, 0.1, L.MA_FLAG_FORCE_DENSE),      # every parameter streamed through registers instead
+    (8192, 0.1, 0),                           # one chunk, decay on the untouched positions
+    (4096, 0.0, 0),
+])
+def test_fused_parameter_write_back_forms(B, wd, flags):
+    # the fused kernel's three forms of the parameter update at m = 10 (fp32,
+    # 16-byte aligned) give the oracle's bits
+    d = 9 * B + 321
+    full_parity(f"fused write-back B={B} wd={wd} flags={flags}", d, B, d // 100, 10, 12, lr=1e-2 if wd else 1e-4,
+                wd=wd, gpu_only_flags=flags)
+
+
+def test_fused_parameters_through_lds_with_nothing_touched():
+    # k = 0: no window entries, so no slot; with decay every parameter of the
+    # LDS chunks is scaled, without it each is written back unchanged
+    full_parity("k=0 decay m=10", 4 * 16384, 16384, 0, 10, 3, lr=1e-2, wd=0.1)
+    full_parity("k=0 m=10", 4 * 16384, 16384, 0, 10, 3)
+
+
 def test_fused_decay_without_error_feedback():
     # the fused kernel's dense update with the error feedback switched off
     full_parity("fused decay no EF", 5 * 16384 + 77, 16384, 900, 6, 8, lr=1e-2, wd=0.1, flags=O.FLAG_NO_EF)
