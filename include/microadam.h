@@ -64,12 +64,12 @@ enum {
                                    (same results) */
 #define MA_FLAG_FORCE_SPARSE 8u /* gather only touched parameters (same results; ignored
                                    when weight decay makes every parameter change) */
-/* Without either flag, full blocks of 16-byte aligned fp32 parameters whose
- * window leaves room in the fused kernel's LDS (m * k_b up to about 2,000
- * entries at B_d = 16384) pass through LDS in one or two chunks: the touched
- * positions are updated there and every parameter line is written back whole.
- * Elsewhere the touched parameters are gathered (no decay) or all of them
- * streamed (decay).  Every form gives the same bits. */
+/* Without either flag, full blocks of 16-byte aligned fp32 parameters with a
+ * short window (m * k_b up to 2048 entries: m <= 12 at k = d/100 and
+ * B_d = 16384) are loaded whole into registers and merged through LDS in
+ * chunks: the touched positions are updated there and every parameter line is
+ * written back whole.  Elsewhere the touched parameters are gathered (no
+ * decay) or all of them streamed (decay).  Every form gives the same bits. */
 #define MA_FLAG_UNFUSED 16u     /* run compress and update as two kernels even where the
                                    fused per-block kernel applies (same results) */
 #define MA_FLAG_ROW_SUMS 64u     /* AdamStats by adding the window rows one at a time into

@@ -637,14 +637,17 @@ ma_ctx *ma_create(int64_t d, int32_t B_d, int64_t k, int32_t m, int32_t b, float
     h->fused_union_words = (int32_t)union_words;
     h->fused_csu_lds = 4 * (union_words + (size_t)kb_max);
     h->fused_csu_ok = h->csu_ok && h->cpt <= 4 && B_d == h->cpt * kChunkSpan && h->fused_csu_lds <= kFusedCsuLdsLimit;
-    // fp32 parameters through LDS in the fused kernel: the whole block or
-    // half of it (more chunks expose the loads of each, measured slower:
-    // LLaMA-2-13B m = 20, four chunks, 32.6 against 30.2 ms), behind the
-    // update's arrays (bitmap, slot bases, decay factors, slots, entries),
-    // 16-byte aligned, within the static buffer
-    const size_t thl_off = (2 * (size_t)W + 2 * (size_t)m + (size_t)csu_slots + (size_t)ents + 3) & ~(size_t)3;
-    if (h->fused_csu_ok)
-      for (int64_t n = B_d; n >= B_d / 2 && n >= 4 * kThreads; n /= 2)
+    // fp32 parameters through LDS in the fused kernel, for windows of at most
+    // four entries per thread (m * k_b <= 2048: m <= 12 at k = d/100 and
+    // B_d = 16384); with longer windows the gather measured faster (LLaMA-2-13B
+    // m = 20: 30.8 against 32.5 ms, m = 37: 39.6 against 42.8).  The chunk:
+    // the largest power-of-two part of the block (at least 4 * kThreads
+    // floats) that fits behind the update's bitmap, slot bases, decay factors
+    // and slots (over the window entries, which are summed by then), 16-byte
+    // aligned, within the static buffer
+    const size_t thl_off = (2 * (size_t)W + 2 * (size_t)m + (size_t)csu_slots + 3) & ~(size_t)3;
+    if (h->fused_csu_ok && ents <= 4 * (int64_t)kThreads)
+      for (int64_t n = B_d; n >= 4 * kThreads; n /= 2)
         if (thl_off + (size_t)n <= (size_t)kFusedCsuWords) {
           h->thl_off = (int32_t)thl_off;
           h->thl_n = (int32_t)n;

@@ -1490,16 +1490,6 @@ __device__ __forceinline__ int csu_row(int x, float inv_kb) {
   return (int)(((float)x + 0.5f) * inv_kb);
 }
 
-// Issues the LDS-DMA of n fp32 parameters from element i0 (16-byte aligned;
-// n a multiple of 4 * kThreads) into R, 16 bytes per lane.  The caller waits
-// for its vector memory and a barrier before R is read.
-__device__ __forceinline__ void stage_theta_chunk(const ApplyArgs &A, float *R, int64_t i0, int n, int tid) {
-  const u32x4 *src = reinterpret_cast<const u32x4 *>(A.theta + i0);
-  u32x4 *dst = reinterpret_cast<u32x4 *>(R);
-  for (int q = tid; q < n / 4; q += kThreads)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + q), (lds_void_t *)(dst + (q & ~63)), 16, 0,
-                                     0);
-}
 
 // MODE as apply_block (kModeSparse, kModeDense, kModeMoments).
 // newrow (optional): window row t mod m of the block, already in LDS (the
@@ -1513,13 +1503,15 @@ __device__ __forceinline__ void stage_theta_chunk(const ApplyArgs &A, float *R, 
 // meanwhile), else after them.  The sparse mode loads each touched parameter
 // before the sums in either case, one word per slot.
 // THL (fp32 parameters, 16-byte aligned, full block; sparse or dense mode):
-// the parameters pass through LDS in chunks of thl_n floats at thl, every
-// 128-byte line read and written whole: each chunk comes in by LDS-DMA (the
-// first one in flight during the sort), the slot threads update their touched
-// positions in LDS (theta * decay - update), and the chunk goes back in
-// coalesced 16-byte stores, the untouched positions scaled by the decay.
-// Whole-line write-back costs less HBM time than the dirty 32-byte sectors of
-// a scattered one, even though it moves every byte.
+// every 128-byte line of the block's parameters is read and written whole.
+// The block's 16-byte groups are loaded into registers before the column
+// sums (as EARLY); after them they pass through LDS in chunks of thl_n floats
+// at thl (over the dead window entries): each chunk is written to LDS, the
+// slot threads update their touched positions there (theta * decay -
+// update), and the chunk goes back in coalesced 16-byte stores, the
+// untouched positions scaled by the decay.  Whole-line write-back costs less
+// HBM time than the dirty 32-byte sectors of a scattered one, even though it
+// moves every byte.
 template <int CPT, int MODE, bool ALIGNED, bool BF = false, bool EARLY = true, bool THL = false>
 __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, int64_t out_row, const CsuSmem &sm,
                                                 const uint32_t *newrow = nullptr, int64_t pre_off = 0,
@@ -1556,8 +1548,6 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
     for (int q = tid; q < kb; q += kThreads) sm.col[A.tm * kb + q] = newrow[q];
   wait_vm_all();
   __syncthreads();
-  // THL: the first parameter chunk, in flight while the window is sorted
-  if (THL) stage_theta_chunk(A, thl, s, A.thl_n, tid);
 
   // ---------------- each thread's entries (x = tid + u * 512) into registers,
   // and the bitmap of the touched positions.  A zero value adds nothing
@@ -1662,9 +1652,9 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
   // every group whole and aligned (uniform over the block): 16-byte loads and
   // stores; otherwise element by element at the end
   const bool vec_all = ALIGNED && (L % G) == 0;
-  u32x4 raw[MODE == kModeDense ? NIT : 1];
+  u32x4 raw[(MODE == kModeDense || THL) ? NIT : 1];
   auto issue_loads = [&]() {
-    if (MODE == kModeDense && !THL) {
+    if (MODE == kModeDense || THL) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         const int i0 = (it * kThreads + tid) * G;
@@ -1675,7 +1665,7 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
       }
     }
   };
-  if (EARLY) issue_loads();
+  if (EARLY || THL) issue_loads();
 
   // ---------------- each slot's column: sorted by row, summed in row order
   // (slots tid, tid + 512, ...).  Sparse mode: the thread that sums a slot
@@ -1780,39 +1770,49 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
     }
   }
   if (THL) {
-    // ---------------- the parameters through LDS, chunk by chunk
+    // ---------------- the parameters through LDS, chunk by chunk: thread t's
+    // groups it (elements 4 (it * 512 + t) ..) go to the chunk's LDS; after
+    // a barrier the slot threads update their positions of the chunk; after
+    // another the chunk is stored.  (it is unrolled: raw[] is indexed by
+    // constants; a chunk holds itc of each thread's groups.)
     const bool decays = A.decay != 1.0f;
     const int cn = A.thl_n;
-    const u32x4 *R4 = reinterpret_cast<const u32x4 *>(thl);
-    for (int c0 = 0; c0 < L; c0 += cn) {
-      if (c0 > 0) stage_theta_chunk(A, thl, s + c0, cn, tid);
-      wait_vm_all();
-      __syncthreads();
+    const int itc = cn / (G * kThreads);   // a power of two
+    u32x4 *R4 = reinterpret_cast<u32x4 *>(thl);
 #pragma unroll
-      for (int u = 0; u < kCsuPerThread; ++u) {
-        if (u < nU) {
-          const uint32_t q = thp[u] - (uint32_t)c0;
-          if (q < (uint32_t)cn) {
-            float th = thl[q];
-            if (decays) th = th * A.decay;
-            thl[q] = th - thu[u];
+    for (int it = 0; it < NIT; ++it) {
+      const int li = it & (itc - 1);
+      if (li == 0) __syncthreads();   // the LDS chunk is free: entries summed, previous chunk stored
+      R4[li * kThreads + tid] = raw[it];
+      if (li == itc - 1) {
+        const int c0 = (it - li) * G * kThreads;   // the chunk's first element
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kCsuPerThread; ++u) {
+          if (u < nU) {
+            const uint32_t q = thp[u] - (uint32_t)c0;
+            if (q < (uint32_t)cn) {
+              float th = thl[q];
+              if (decays) th = th * A.decay;
+              thl[q] = th - thu[u];
+            }
           }
         }
-      }
-      __syncthreads();
-      for (int q = tid; q < cn / 4; q += kThreads) {
-        u32x4 v = R4[q];
-        if (decays) {
-          const int i0 = c0 + 4 * q;
-          const uint32_t gb = (sm.bits[i0 >> 5] >> (i0 & 31)) & 15u;   // touched ones are already done
-          if (!(gb & 1u)) v.x = f2u(u2f(v.x) * A.decay);
-          if (!(gb & 2u)) v.y = f2u(u2f(v.y) * A.decay);
-          if (!(gb & 4u)) v.z = f2u(u2f(v.z) * A.decay);
-          if (!(gb & 8u)) v.w = f2u(u2f(v.w) * A.decay);
+        __syncthreads();
+        for (int r = 0; r < itc; ++r) {
+          const int q = r * kThreads + tid;
+          u32x4 v = R4[q];
+          if (decays) {
+            const int i0 = c0 + G * q;
+            const uint32_t gb = (sm.bits[i0 >> 5] >> (i0 & 31)) & 15u;   // touched ones are already done
+            if (!(gb & 1u)) v.x = f2u(u2f(v.x) * A.decay);
+            if (!(gb & 2u)) v.y = f2u(u2f(v.y) * A.decay);
+            if (!(gb & 4u)) v.z = f2u(u2f(v.z) * A.decay);
+            if (!(gb & 8u)) v.w = f2u(u2f(v.w) * A.decay);
+          }
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(A.theta + s + c0) + q);
         }
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(A.theta + s + c0) + q);
       }
-      if (c0 + cn < L) __syncthreads();   // the next chunk's loads overwrite the LDS chunk
     }
     if (A.touched && tid == 0) atomicAdd(A.touched + (j & (kTouchedSlots - 1)), (unsigned long long)U);
     return;
