@@ -213,6 +213,22 @@ int ma_read_state(const ma_ctx *h, int which, uint64_t byte_offset, uint64_t nby
 int ma_write_state(ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, const void *host_src);
 
 /*
+ * The whole optimizer state in one call, for checkpoint and exact resume (the
+ * state the second paragraph of the MicroAdam page counts, plus the block
+ * statistics and the step count; the quantizer's random numbers are keyed on
+ * (seed, step, element), so these determine every later step).  Host buffers
+ * the caller owns: codes ceil(d/2) bytes (element i in nibble i), stats 8*n_b
+ * bytes (fp32 delta, Delta per block), window 4*m*k bytes (row-major m x k
+ * entries, int16 index | bf16 value << 16); t the number of completed steps.
+ * window may be NULL when m*k = 0.  Synchronous: waits for the device first.
+ * MA_EINVAL for a null handle or buffer, or t < 0 on import; MA_EHIP if a copy
+ * fails, after which an imported state is incomplete and must be imported
+ * again before the next step.
+ */
+int ma_export_state(const ma_ctx *h, void *codes, void *stats, void *window, int64_t *t);
+int ma_import_state(ma_ctx *h, const void *codes, const void *stats, const void *window, int64_t t);
+
+/*
  * m_hat and v_hat of the last completed step (AdamStats of the first
  * paragraph, bias-corrected) for nblocks chosen blocks.  blocks: host array of
  * block numbers.  mhat_out, vhat_out: device f32[nblocks * B_d]; row q holds

@@ -1121,6 +1121,31 @@ int ma_write_state(ma_ctx *h, int which, uint64_t byte_offset, uint64_t nbytes, 
   return MA_OK;
 }
 
+int ma_export_state(const ma_ctx *h, void *codes, void *stats, void *window, int64_t *t) {
+  clear_error();
+  if (!h || !codes || !stats || !t) return fail(MA_EINVAL, "ma_export_state: null argument");
+  const uint64_t wbytes = 4ull * h->m * h->k;
+  if (wbytes && !window) return fail(MA_EINVAL, "ma_export_state: null window buffer");
+  int rc = ma_read_state(h, MA_STATE_CODES, 0, h->codes_bytes, codes);
+  if (rc == MA_OK) rc = ma_read_state(h, MA_STATE_STATS, 0, 8ull * h->n_b, stats);
+  if (rc == MA_OK && wbytes) rc = ma_read_state(h, MA_STATE_WINDOW, 0, wbytes, window);
+  if (rc == MA_OK) *t = h->t;
+  return rc;
+}
+
+int ma_import_state(ma_ctx *h, const void *codes, const void *stats, const void *window, int64_t t) {
+  clear_error();
+  if (!h || !codes || !stats) return fail(MA_EINVAL, "ma_import_state: null argument");
+  if (t < 0) return fail(MA_EINVAL, "ma_import_state: negative step");
+  const uint64_t wbytes = 4ull * h->m * h->k;
+  if (wbytes && !window) return fail(MA_EINVAL, "ma_import_state: null window buffer");
+  int rc = ma_write_state(h, MA_STATE_CODES, 0, h->codes_bytes, codes);
+  if (rc == MA_OK) rc = ma_write_state(h, MA_STATE_STATS, 0, 8ull * h->n_b, stats);
+  if (rc == MA_OK && wbytes) rc = ma_write_state(h, MA_STATE_WINDOW, 0, wbytes, window);
+  if (rc == MA_OK) h->t = t;
+  return rc;
+}
+
 int ma_debug_moments(ma_ctx *h, const int64_t *blocks, int64_t nblocks, float *mhat_out, float *vhat_out,
                      hipStream_t stream) {
   clear_error();

@@ -121,14 +121,28 @@ class MicroAdam:
         return self.read_state(_L.MA_STATE_WINDOW, 4 * offset, 4 * n).view(np.uint32)
 
     def export_state(self) -> dict:
-        return {"codes": self.codes_bytes(), "stats": self.stats(), "window": self.window(), "t": self.t}
+        """The whole state (ma_export_state): codes, block statistics, window, t."""
+        codes = np.empty((self.d + 1) // 2, np.uint8)
+        stats = np.empty(2 * self.num_blocks, np.float32)
+        window = np.empty(self.m * self.k, np.uint32)
+        t = C.c_int64(0)
+        _L.check(_L.lib().ma_export_state(self._h, codes.ctypes.data_as(C.c_void_p),
+                                          stats.ctypes.data_as(C.c_void_p),
+                                          window.ctypes.data_as(C.c_void_p) if window.size else None,
+                                          C.byref(t)))
+        return {"codes": codes, "stats": stats, "window": window, "t": int(t.value)}
 
     def import_state(self, st: dict):
-        self.write_state(_L.MA_STATE_CODES, 0, st["codes"])
-        self.write_state(_L.MA_STATE_STATS, 0, st["stats"])
-        if self.m * self.k:
-            self.write_state(_L.MA_STATE_WINDOW, 0, st["window"])
-        self.set_step(st["t"])
+        """Restores a state from export_state (ma_import_state)."""
+        codes = np.ascontiguousarray(st["codes"], np.uint8)
+        stats = np.ascontiguousarray(st["stats"], np.float32)
+        window = np.ascontiguousarray(st["window"], np.uint32)
+        _L.require(codes.size == (self.d + 1) // 2 and stats.size == 2 * self.num_blocks
+                   and window.size == self.m * self.k, "state buffers of the wrong size")
+        _L.check(_L.lib().ma_import_state(self._h, codes.ctypes.data_as(C.c_void_p),
+                                          stats.ctypes.data_as(C.c_void_p),
+                                          window.ctypes.data_as(C.c_void_p) if window.size else None,
+                                          int(st["t"])))
 
     def moments(self, blocks, stream=None):
         """(m_hat, v_hat) of the last step for the given blocks, as CUDA

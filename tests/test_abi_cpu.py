@@ -67,6 +67,8 @@ def test_null_handles_are_safe():
     assert lib.ma_step(None, None, None, None) == L.MA_EINVAL
     assert lib.ma_set_flags(None, 0) == L.MA_EINVAL
     assert lib.ma_read_state(None, 0, 0, 0, None) == L.MA_EINVAL
+    assert lib.ma_export_state(None, None, None, None, None) == L.MA_EINVAL
+    assert lib.ma_import_state(None, None, None, None, 0) == L.MA_EINVAL
     assert lib.ma_kernel_times(None, None, None, 0) == L.MA_EINVAL
     assert lib.ma_set_pipeline(None, 4) == L.MA_EINVAL
     assert lib.ma_debug_residual(None, None, None, 0, None, None) == L.MA_EINVAL

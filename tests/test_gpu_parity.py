@@ -389,9 +389,15 @@ def test_export_import_resume():
         a.step(ta, to_gpu_bf16(grads[t]))
     torch.cuda.synchronize()
     st = a.export_state()
+    # the one-call export (ma_export_state) equals the buffer-by-buffer reads
+    assert st["t"] == 4
+    np.testing.assert_array_equal(st["codes"], a.codes_bytes())
+    np.testing.assert_array_equal(st["stats"].view(np.uint32), a.stats().view(np.uint32))
+    np.testing.assert_array_equal(st["window"], a.window())
     tb = ta.clone()
     b = MicroAdam(d, B, k, m)
     b.import_state(st)
+    assert b.t == 4
     say("[resume] continuing both runs for 4 steps")
     for t in range(4, 8):
         a.step(ta, to_gpu_bf16(grads[t]))
