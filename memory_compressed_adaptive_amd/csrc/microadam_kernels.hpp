@@ -1775,6 +1775,9 @@ __device__ __forceinline__ void apply_block_csu(const ApplyArgs &A, int64_t j, i
     // a barrier the slot threads update their positions of the chunk; after
     // another the chunk is stored.  (it is unrolled: raw[] is indexed by
     // constants; a chunk holds itc of each thread's groups.)
+    // (THL runs for full, aligned blocks only, so vec_all holds and every
+    // group was loaded; the host sizes thl_n as a power-of-two part of the
+    // block of at least G * kThreads elements, so itc >= 1)
     const bool decays = A.decay != 1.0f;
     const int cn = A.thl_n;
     const int itc = cn / (G * kThreads);   // a power of two
@@ -2064,7 +2067,9 @@ __global__ __launch_bounds__(kThreads, MA_FULL_WAVES) void step_full_kernel(Comp
 // beside its global copy.  Co-resident workgroups are in different phases, so
 // the arithmetic-bound compressor and the memory-bound update share each CU.
 // Blocks the compressor defers are left to compress_deferred_kernel and
-// apply_csu_list_kernel, as in step_full_kernel.
+// apply_csu_list_kernel, as in step_full_kernel.  THL: the update writes every
+// parameter line whole, through an LDS chunk at A.thl_off words (behind the
+// update's slot words, over its dead window entries; apply_block_csu).
 // (A static buffer: with a dynamic one the compressor's addresses are formed
 // at run time and its registers spill.)  Three workgroups fit a CU's 160 KiB
 // when each takes at most 53,760 bytes (LDS is allocated in 1,280-byte
