@@ -547,22 +547,23 @@ def _nonfinite_grads(B):
     return fn
 
 
-@pytest.mark.parametrize("B,flags,gq,wd", [
-    (16384, 0, False, 0.0),                  # fused kernel (and the blocks it defers)
-    (16384, L.MA_FLAG_UNFUSED, False, 0.0),  # two kernels
-    (16384, 0, True, 0.0),                   # one (delta, Delta) over all d
-    (16384, 0, False, 0.1),                  # dense update with decay
-    (1003, 0, False, 0.0),                   # odd B_d: the general compressor
-    (4096, L.MA_FLAG_NO_EF, False, 0.0),     # no error feedback: a = widened g, signalling NaNs kept
+@pytest.mark.parametrize("B,flags,gq,wd,m", [
+    (16384, 0, False, 0.0, 4),                  # fused kernel (and the blocks it defers)
+    (16384, 0, False, 0.0, 10),                 # fused, parameter lines written whole
+    (16384, L.MA_FLAG_UNFUSED, False, 0.0, 4),  # two kernels
+    (16384, 0, True, 0.0, 4),                   # one (delta, Delta) over all d
+    (16384, 0, False, 0.1, 4),                  # dense update with decay
+    (1003, 0, False, 0.0, 4),                   # odd B_d: the general compressor
+    (4096, L.MA_FLAG_NO_EF, False, 0.0, 4),     # no error feedback: a = widened g, signalling NaNs kept
 ])
-def test_nonfinite_gradients(B, flags, gq, wd):
+def test_nonfinite_gradients(B, flags, gq, wd, m):
     # the reading for non-finite values: NaN and +-Inf are selected first (NaN
     # canonical), what is left is dropped from the error feedback, a range with
     # no finite value resets it; window, codes and statistics bit-exact, the
     # parameters NaN where the oracle's are
     d = 7 * B + 777 if B >= 4096 else 60 * B + 17
     oflags = (O.FLAG_NO_EF if flags & L.MA_FLAG_NO_EF else 0)
-    full_parity(f"non-finite B={B} flags={flags} global={gq} wd={wd}", d, B, d // 100, 4, 5,
+    full_parity(f"non-finite B={B} flags={flags} global={gq} wd={wd} m={m}", d, B, d // 100, m, m + 1,
                 lr=1e-2 if wd else 1e-4, wd=wd, flags=oflags, gpu_only_flags=flags & ~L.MA_FLAG_NO_EF,
                 grad_fn=_nonfinite_grads(B), global_quant=gq)
 
@@ -584,8 +585,8 @@ def _tiny_grads(kind):
 
 
 @pytest.mark.parametrize("kind", ["mixed", "subnormal"])
-@pytest.mark.parametrize("m,row_sums,wd", [(4, False, 0.0), (4, True, 0.0), (4, False, 0.1), (20, False, 0.0),
-                                           (20, False, 0.1)])
+@pytest.mark.parametrize("m,row_sums,wd", [(4, False, 0.0), (4, True, 0.0), (4, False, 0.1), (10, False, 0.0),
+                                           (20, False, 0.0), (20, False, 0.1)])
 def test_tiny_gradients_square_root_paths(kind, m, row_sums, wd):
     # the update's correctly rounded square root: its fast path where a wave's
     # v_hat are all in [2^-96, FLT_MAX], sqrtf otherwise; both equal the
