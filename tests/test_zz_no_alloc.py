@@ -75,6 +75,13 @@ def test_noalloc_step_equals_step_fused_then_smaller():
     _run("fused, smaller", 3 * 16384 + 77, 16384, (3 * 16384 + 77) // 100, 4, 5, grad_fn=_tied, seed=1)
 
 
+def test_noalloc_step_equals_step_whole_line_write_back():
+    # m = 10: the fused column-sorted kernel writes every parameter line whole
+    # (with deferred blocks), then with decay on a smaller set
+    _run("whole lines", 6 * 16384 + 1234, 16384, (6 * 16384 + 1234) // 100, 10, 12, grad_fn=_tied)
+    _run("whole lines, decay, smaller", 3 * 16384 + 77, 16384, (3 * 16384 + 77) // 100, 10, 11, wd=0.1, seed=3)
+
+
 def test_noalloc_step_equals_step_two_kernels_and_global():
     # a long window (two kernels, one block range) with decay, then the global
     # quantizer (per-block partials in the scratch) on a smaller set, fused
