@@ -905,25 +905,46 @@ int step_impl(ma_ctx *h, void *params, bool bf, const uint16_t *grads, hipStream
   }
 
   // Fused path: every full block runs compress and update in one workgroup;
-  // a partial last block (if any) runs the two kernels after it.  The dense
-  // update (decoupled decay) is fused for 16-byte aligned parameters.
+  // a partial last block (if any) runs the two kernels, on the library's
+  // side stream concurrently with the fused kernel (its block, window segment
+  // and parameters are its own; the side stream joins the caller's before
+  // ma_step returns), or after it on the caller's stream for the
+  // no-allocation entry point.  The dense update (decoupled decay) is fused
+  // for 16-byte aligned parameters.
   if ((ul.fused_csu || h->fused_ok) && n_full > 0 && (mode == kModeSparse || p_al) && !(h->flags & MA_FLAG_UNFUSED)) {
+    const bool part = n_full < h->n_b;
+    const bool beside = part && !noalloc;
+    if (beside && !ensure_pipeline(h, 1)) return fail(MA_EHIP, "ma_step: creating the side stream failed");
     hipEvent_t tf[2] = {};
     if (timing && !take_events(h, tf, 2)) return fail(MA_EHIP, "ma_step: hipEventCreate failed");
     hipEvent_t t0 = tf[0], t1 = tf[1];
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, 1);
-    e = hipGetLastError();
+    ApplyArgs at = aa;
+    at.first_block = n_full;
+    hipStream_t ps = beside ? h->side : stream;   // the partial block's stream
+    if (beside) {
+      e = hipEventRecord(h->fork_ev, stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork_ev, 0);
+      if (e == hipSuccess) e = dispatch_compress(h->cpt, g_al, ef, ca, n_full, h->n_b, n_full, ps);
+      if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, ul, ps, bf);
+    }
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, q_counts, 1);
+      e = hipGetLastError();
+    }
     if (t0) (void)hipEventRecord(t0, stream);
     if (e == hipSuccess) e = dispatch_fused(h->cpt, ef, mode == kModeDense, p_al, ca, aa, n_full, ul, stream, bf);
     if (t1) {
       (void)hipEventRecord(t1, stream);
       h->events.push_back({2, t0, t1});
     }
-    if (e == hipSuccess && n_full < h->n_b) {
+    if (e == hipSuccess && part && !beside) {
       e = dispatch_compress(h->cpt, g_al, ef, ca, n_full, h->n_b, n_full, stream);
-      ApplyArgs at = aa;
-      at.first_block = n_full;
       if (e == hipSuccess) e = dispatch_apply(h->cpt, mode, p_al, at, h->n_b - n_full, ul, stream, bf);
+    }
+    if (beside) {
+      hipError_t e2 = hipEventRecord(h->join_ev, h->side);
+      if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, h->join_ev, 0);
+      if (e == hipSuccess) e = e2;
     }
     if (e != hipSuccess) return fail(MA_EHIP, "ma_step: kernel launch failed: %s", hipGetErrorString(e));
     h->t = t;
